@@ -1,0 +1,253 @@
+"""Pins for the CPU oracle against what the Sherry page and mathematics fix.
+
+Each test checks the oracle against something other than itself: brute force
+over all candidates, exhaustive joint search, a numeric line search, the
+page's worked block, hand-derived golden bytes, exact library arithmetic
+(torch float64 matmul is exact on these integers), invariants stated on the
+page (values in {-1,0,1}; exactly 3 nonzeros per block), or closed forms.
+"""
+
+import itertools
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from bit_weight_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# All 32 blocks with exactly three nonzeros in {-1,+1}, enumerated here
+# independently of the oracle's pattern table.
+ALL32 = np.array([v for v in itertools.product((-1, 0, 1), repeat=4)
+                  if sum(1 for e in v if e != 0) == 3], dtype=np.int8)
+
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split(":", 1)
+            out.setdefault(key.strip(), []).append(val.split())
+    return out
+
+
+def test_all32_has_32():
+    assert ALL32.shape == (32, 4)
+
+
+def test_patterns_are_canonical(orc):
+    seen = set()
+    for p in range(16):
+        v = orc.pattern(p)
+        nz = v[v != 0]
+        assert nz.size == 3 and set(v.tolist()) <= {-1, 0, 1}
+        assert nz[0] == 1, "canonical pattern: first nonzero is +1"
+        seen.add(tuple(v.tolist()))
+    assert len(seen) == 16
+
+
+def test_codes_are_a_bijection_onto_all32(orc):
+    dec = np.stack([orc.decode_code(c) for c in range(32)])
+    assert {tuple(r) for r in dec.tolist()} == {tuple(r) for r in ALL32.tolist()}
+    for c in range(32):
+        assert orc.encode_block(dec[c]) == c
+        # sign bit is the lowest bit: code 2p+1 is the negation of code 2p
+        if c % 2 == 0:
+            assert np.array_equal(dec[c + 1], -dec[c])
+            assert np.array_equal(dec[c], orc.pattern(c // 2))
+
+
+def test_encode_rejects_non_34_blocks(orc):
+    for bad in ([0, 0, 1, 1], [1, 1, 1, 1], [2, 0, 1, 1], [0, 1, -1, 3], [0, 0, 0, 0]):
+        assert orc.encode_block(bad) == -1
+
+
+def test_worked_block_from_page(orc):
+    g = _golden("worked_block.txt")
+    block = np.array([float(v) for v in g["block"][0]], np.float32)
+    W = np.tile(block, 32)[None, :]          # one row, K = 128
+    T, alpha = orc.quantize(W)
+    assert np.array_equal(T[0, :4], block.astype(np.int8))
+    assert alpha[0] == np.float32(float(g["alpha"][0][0]))
+    c = orc.encode_block(block.astype(np.int8))
+    assert c == int(g["code"][0][0])
+    assert c == 2 * int(g["p"][0][0]) + int(g["s"][0][0])
+
+
+def _random_blocks(n, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0, 1, size=(n, 4)).astype(np.float32)
+    # ties and special values: repeated magnitudes, zeros, spikes
+    w[: n // 10] = np.round(w[: n // 10])
+    w[n // 10: n // 5] = rng.choice([-5.0, 5.0, 0.0, 0.1, -0.1], size=(n // 10, 4))
+    return w
+
+
+def test_quantizer_attains_bruteforce_optimum_per_block(orc):
+    w = _random_blocks(20000, 1)
+    T, _ = orc.quantize(w.reshape(-1, 4))            # each block its own row
+    assert np.all((T != 0).sum(1) == 3)
+    w64 = w.astype(np.float64)
+    best = (w64 @ ALL32.T.astype(np.float64)).max(1)
+    got = (w64 * T).sum(1)
+    np.testing.assert_allclose(got, best, rtol=0, atol=1e-12)
+
+
+def test_quantizer_tie_rule_drops_lowest_index_minimum(orc):
+    w = _random_blocks(5000, 2)
+    T, _ = orc.quantize(w)
+    a = np.abs(w)
+    zero_pos = np.argmax(T == 0, axis=1)
+    first_min = np.argmax(a == a.min(1, keepdims=True), axis=1)
+    assert np.array_equal(zero_pos, first_min)
+
+
+def test_equal_spikes_and_signed_zero(orc):
+    T, alpha = orc.quantize(np.array([[5.0, -5.0, 5.0, -5.0]], np.float32))
+    assert T.tolist() == [[0, -1, 1, -1]] and alpha[0] == 5.0
+    T, alpha = orc.quantize(np.array([[0.0, -0.0, -0.0, -0.0]], np.float32))
+    assert T.tolist() == [[0, 1, 1, 1]] and alpha[0] == 0.0
+
+
+@pytest.mark.parametrize("B,rows", [(2, 40), (3, 4)])
+def test_joint_exhaustive_search_tiny_rows(orc, B, rows):
+    """Per-row alpha: the closed form attains the minimum of ||W - aT||^2 over
+    every combination of exactly-3-nonzero blocks, each with its best a."""
+    rng = np.random.default_rng(10 + B)
+    combos = np.array([np.concatenate(c) for c in itertools.product(ALL32, repeat=B)],
+                      dtype=np.float64)                     # [32^B, 4B]
+    tt = (combos * combos).sum(1)                           # = 3B
+    for _ in range(rows):
+        W = rng.normal(0, 1, size=(1, 4 * B)).astype(np.float32)
+        T, alpha = orc.quantize(W)
+        w = W[0].astype(np.float64)
+        wt = combos @ w
+        err_min = (w @ w - wt * wt / tt).min()
+        err_or = ((w - float(alpha[0]) * T[0]) ** 2).sum()
+        assert err_or <= err_min + 1e-6 * (w @ w)
+
+
+def test_alpha_matches_numeric_line_search(orc):
+    rng = np.random.default_rng(3)
+    W = rng.normal(0, 0.02, size=(8, 256)).astype(np.float32)
+    T, alpha = orc.quantize(W)
+    for n in range(8):
+        w, t = W[n].astype(np.float64), T[n].astype(np.float64)
+        f = lambda a: ((w - a * t) ** 2).sum()
+        lo, hi = 0.0, float(np.abs(w).max())
+        gr = (np.sqrt(5) - 1) / 2
+        for _ in range(200):
+            a1, a2 = hi - gr * (hi - lo), lo + gr * (hi - lo)
+            if f(a1) < f(a2):
+                hi = a2
+            else:
+                lo = a1
+        assert abs(alpha[n] - (lo + hi) / 2) <= 1e-6 * alpha[n]
+
+
+def test_pack_roundtrip_and_size(orc):
+    rng = np.random.default_rng(4)
+    for N, K in [(64, 128), (128, 384), (192, 256)]:
+        codes = rng.integers(0, 32, size=(N, K // 4))
+        T = ALL32[codes].reshape(N, K)
+        P = orc.pack(T)
+        assert P.size == N * K * 5 // 32
+        assert np.array_equal(orc.unpack(P, N, K), T)
+
+
+def test_pack_golden_layout(orc):
+    g = _golden("packed_layout_64x128.txt")
+    T = np.tile(np.array([0, 1, 1, 1], np.int8), (64, 32))
+    for row, blk in ([int(a) for a in v] for v in g["special"]):
+        T[row, 4 * blk: 4 * blk + 4] = [-1, 0, 1, -1]
+    want = np.zeros(64 * 128 * 5 // 32, np.uint8)
+    for off, val in g["byte"]:
+        want[int(off)] = int(val, 16)
+    assert np.array_equal(orc.pack(T), want)
+
+
+def test_lut_equals_direct_dot_and_negation_symmetry(orc):
+    q = synth.int8_uniform(3, 64, seed=5).numpy()
+    L = orc.lut(q)
+    for m in range(3):
+        for seg in range(16):
+            x = q[m, 4 * seg: 4 * seg + 4].astype(np.int64)
+            for v in ALL32:
+                c = orc.encode_block(v)
+                p, s = c >> 1, c & 1
+                val = -L[m, seg, p] if s else L[m, seg, p]
+                assert val == int((v.astype(np.int64) * x).sum())
+
+
+def test_gemm_int32_equals_exact_float64_matmul(orc):
+    rng = np.random.default_rng(6)
+    q = synth.int8_uniform(7, 512, seed=6).numpy()
+    T = ALL32[rng.integers(0, 32, size=(96, 128))].reshape(96, 512)
+    acc = orc.gemm_i32(q, T)
+    ref = torch.from_numpy(q).double() @ torch.from_numpy(T).double().T
+    assert np.array_equal(acc, ref.numpy().astype(np.int64))
+
+
+def test_gemm_one_hot_and_constant_rows(orc):
+    rng = np.random.default_rng(7)
+    K = 256
+    T = ALL32[rng.integers(0, 32, size=(64, K // 4))].reshape(64, K)
+    for k in (0, 1, 131, K - 1):
+        e = np.zeros((1, K), np.int8)
+        e[0, k] = 1
+        assert np.array_equal(orc.gemm_i32(e, T)[0], T[:, k].astype(np.int32))
+    c = np.full((1, K), 127, np.int8)
+    assert np.array_equal(orc.gemm_i32(c, T)[0], 127 * T.astype(np.int32).sum(1))
+    c = np.full((1, K), -128, np.int8)
+    assert np.array_equal(orc.gemm_i32(c, T)[0], -128 * T.astype(np.int32).sum(1))
+
+
+def test_epilogue_within_two_ulp_of_exact(orc):
+    rng = np.random.default_rng(8)
+    acc = rng.integers(-1_000_000, 1_000_000, size=(5, 300)).astype(np.int32)
+    s = rng.uniform(0.001, 0.1, size=5).astype(np.float32)
+    a = rng.uniform(0.001, 0.1, size=300).astype(np.float32)
+    y = orc.epilogue(acc, s, a)
+    exact = (acc.astype(np.float64) * s[:, None].astype(np.float64)
+             * a[None, :].astype(np.float64)).astype(np.float32)
+    ulp = np.spacing(np.abs(exact))
+    assert np.all(np.abs(y.astype(np.float64) - exact) <= 2 * ulp)
+
+
+def test_act_quant_golden_ties(orc):
+    g = _golden("act_quant_ties.txt")
+    x = np.array([[float(v) for v in g["x"][0]]], np.float32)
+    q, s = orc.act_quant(x)
+    assert s[0] == np.float32(float(g["s"][0][0]))
+    assert q[0].tolist() == [int(v) for v in g["q"][0]]
+
+
+def test_act_quant_properties(orc):
+    x = synth.activations(6, 1000, seed=9, outlier_channels=True).numpy()
+    x[5] = 0.0
+    q, s = orc.act_quant(x)
+    assert s[5] == 1.0 and not q[5].any()
+    for m in range(5):
+        amax = np.abs(x[m]).max()
+        assert s[m] == np.float32(amax / np.float32(127.0))
+        assert q[m].min() >= -127 and q[m].max() <= 127
+        assert abs(int(q[m][np.argmax(np.abs(x[m]))])) == 127
+        err = np.abs(x[m].astype(np.float64) - q[m] * np.float64(s[m]))
+        assert np.all(err <= 0.5 * s[m] * (1 + 1e-5))
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_every_block_has_three_nonzeros_on_workload_data(orc, name):
+    w = synth.WORKLOADS[name]
+    W = synth.weights(64, w.K, w.w_std, w.w_spikes, w.seed_w).numpy()
+    T, alpha = orc.quantize(W)
+    # the page's diagnostic: histogram over bins [-1.5,-0.5,0.5,1.5] holds all
+    hist, _ = np.histogram(T, bins=[-1.5, -0.5, 0.5, 1.5])
+    assert hist.sum() == T.size
+    assert np.all((T.reshape(64, -1, 4) != 0).sum(-1) == 3)
+    assert np.all(alpha > 0)
