@@ -1,1 +1,226 @@
-"""Sherry 3:4-sparse ternary matmul for MI355X (gfx950)."""
+"""Sherry 3:4-sparse ternary matmul for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``libsherry.so`` (declared in
+``include/sherry.h``).  The functions here only check tensors, allocate
+outputs with PyTorch and pass raw device pointers and the current HIP stream;
+every step of the computation runs in the library's HIP kernels.  There is no
+CPU fallback: if the library is missing, every call raises.
+
+Method: the page "Sherry框架：三元量化与3:4稀疏优化LLM推理" (pnsm.cn) --
+ternary weights with exactly three nonzeros per block of four (§1.1), 5-bit
+codes (§2.1), per-segment lookup tables with one float rescale (§2.2), top-3
+ternarization (§3.1).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "SherryError", "lib", "packed_bytes", "workspace_bytes", "plan",
+    "quantize_pack", "quantize_act", "gemm", "gemm_i32", "linear",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsherry.so")
+
+STATUS = {
+    0: "SHERRY_OK", -1: "SHERRY_ERR_NULL", -2: "SHERRY_ERR_SHAPE",
+    -3: "SHERRY_ERR_ALIGN", -4: "SHERRY_ERR_WORKSPACE", -5: "SHERRY_ERR_HIP",
+    -6: "SHERRY_ERR_DEVICE",
+}
+
+
+class SherryError(RuntimeError):
+    """A non-zero status from libsherry."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = lib().sherry_status_string(status).decode()
+        super().__init__(f"{what}: {msg} ({status})")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsherry.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m bit_weight_amd.build` (or __graft_entry__.build())")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i64, sz, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+            ip = ctypes.POINTER(ctypes.c_int)
+            sigs = {
+                "sherry_status_string": ([ci], ctypes.c_char_p),
+                "sherry_packed_bytes": ([i64, i64], sz),
+                "sherry_workspace_bytes": ([i64, i64, i64], sz),
+                "sherry_gemm_plan": ([i64, i64, i64, ip, ip, ip, ip, ip], ci),
+                "sherry_quantize_pack": ([vp, i64, i64, vp, vp, vp], ci),
+                "sherry_quantize_act": ([vp, i64, i64, vp, vp, vp], ci),
+                "sherry_gemm": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
+                "sherry_gemm_i32": ([vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
+            }
+            for name, (args, res) in sigs.items():
+                fn = getattr(L, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise SherryError(status, what)
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise RuntimeError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise RuntimeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def packed_bytes(N: int, K: int) -> int:
+    """Bytes of the packed format for an [N,K] weight matrix (N*K*5/32)."""
+    return int(lib().sherry_packed_bytes(N, K))
+
+
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    """Scratch bytes sherry_gemm needs for this shape."""
+    return int(lib().sherry_workspace_bytes(M, N, K))
+
+
+def plan(M: int, N: int, K: int) -> dict:
+    """Launch plan of the product for a shape (path, grid, block, splits, LDS)."""
+    vals = [ctypes.c_int() for _ in range(5)]
+    _check(lib().sherry_gemm_plan(M, N, K, *[ctypes.byref(v) for v in vals]), "sherry_gemm_plan")
+    path, grid, block, splits, lds = (v.value for v in vals)
+    return {"path": "lut_gemv" if path == 0 else "decode_mfma", "grid": grid,
+            "block": block, "splits": splits, "lds_bytes": lds}
+
+
+def quantize_pack(W: torch.Tensor):
+    """Offline compression of fp32 weights [N,K] -> (packed uint8, alpha fp32 [N])."""
+    pW = _dev_tensor(W, "W", torch.float32)
+    if W.dim() != 2:
+        raise RuntimeError("W must be 2-D [N,K]")
+    N, K = W.shape
+    nb = packed_bytes(N, K)
+    if nb == 0:
+        raise SherryError(-2, "sherry_quantize_pack")
+    packed = torch.empty(nb, dtype=torch.uint8, device=W.device)
+    alpha = torch.empty(N, dtype=torch.float32, device=W.device)
+    _check(lib().sherry_quantize_pack(pW, N, K, packed.data_ptr(), alpha.data_ptr(),
+                                      _stream(W.device)), "sherry_quantize_pack")
+    return packed, alpha
+
+
+def quantize_act(x: torch.Tensor):
+    """Per-token int8 quantization of fp32 activations [M,K] -> (q int8, s_x fp32 [M])."""
+    px = _dev_tensor(x, "x", torch.float32)
+    if x.dim() != 2:
+        raise RuntimeError("x must be 2-D [M,K]")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().sherry_quantize_act(px, M, K, q.data_ptr(), s.data_ptr(), _stream(x.device)),
+           "sherry_quantize_act")
+    return q, s
+
+
+class _Workspaces:
+    """Zero-filled scratch per (device, stream), grown on demand.
+
+    The library leaves a workspace zero-ready after every call, so one buffer
+    serves every call issued on its stream."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, device: torch.device, nbytes: int):
+        if nbytes == 0:
+            return None
+        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+        buf = self._bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            self._bufs[key] = buf
+        return buf
+
+
+_workspaces = _Workspaces()
+
+
+def _gemm_args(x, packed, N, K):
+    px = _dev_tensor(x, "x", torch.int8)
+    _dev_tensor(packed, "packed", torch.uint8)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise RuntimeError(f"x must be [M,{K}]")
+    if packed.numel() != packed_bytes(N, K):
+        raise RuntimeError("packed has the wrong size for [N,K]")
+    M = x.shape[0]
+    ws = _workspaces.get(x.device, workspace_bytes(M, N, K))
+    return px, M, ws
+
+
+def gemm(x: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor,
+         N: int, K: int, out: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M,N] = ((float)(x_int8 @ T^T) * s_x[:,None]) * alpha[None,:]."""
+    px, M, ws = _gemm_args(x, packed, N, K)
+    _dev_tensor(s_x, "s_x", torch.float32)
+    _dev_tensor(alpha, "alpha", torch.float32)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    py = _dev_tensor(out, "out", torch.float32)
+    if workspace is not None:
+        ws = workspace
+    wp = ws.data_ptr() if ws is not None else None
+    wn = ws.numel() if ws is not None else 0
+    _check(lib().sherry_gemm(px, s_x.data_ptr(), packed.data_ptr(), alpha.data_ptr(), py, M, N, K,
+                             wp, wn, _stream(x.device)), "sherry_gemm")
+    return out
+
+
+def gemm_i32(x: torch.Tensor, packed: torch.Tensor, N: int, K: int,
+             out: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """acc[M,N] = x_int8 @ T^T in int32 (exact)."""
+    px, M, ws = _gemm_args(x, packed, N, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    pa = _dev_tensor(out, "out", torch.int32)
+    if workspace is not None:
+        ws = workspace
+    wp = ws.data_ptr() if ws is not None else None
+    wn = ws.numel() if ws is not None else 0
+    _check(lib().sherry_gemm_i32(px, packed.data_ptr(), pa, M, N, K, wp, wn, _stream(x.device)),
+           "sherry_gemm_i32")
+    return out
+
+
+def linear(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, N: int, K: int):
+    """fp32 activations [M,K] -> y [M,N]: per-token int8 quantization then the product."""
+    q, s = quantize_act(x)
+    return gemm(q, s, packed, alpha, N, K)

@@ -1,0 +1,137 @@
+// Kernel 1 (offline compression) and the activation quantizer.
+//
+// [Sherry page §3.1] each 4-weight block keeps its three largest |w| with
+// their signs; [§2.1] the result is stored as a 5-bit code (4-bit pattern
+// index + sign bit).  The per-row scale is the least-squares value for the
+// chosen T: (sum of kept |w|) / (number of kept weights).
+#include "sherry_device.h"
+#include "sherry_launch.h"
+
+namespace sherry {
+namespace {
+
+// Code of one block of four weights: drop the first smallest |w|, keep the
+// signs of the rest (w < 0 -> -1, else +1).
+__device__ __forceinline__ uint32_t encode_block(float w0, float w1, float w2, float w3) {
+  const float a0 = fabsf(w0), a1 = fabsf(w1), a2 = fabsf(w2), a3 = fabsf(w3);
+  int z = 0;
+  float amin = a0;
+  if (a1 < amin) { z = 1; amin = a1; }
+  if (a2 < amin) { z = 2; amin = a2; }
+  if (a3 < amin) { z = 3; }
+  const uint32_t n0 = w0 < 0.0f, n1 = w1 < 0.0f, n2 = w2 < 0.0f, n3 = w3 < 0.0f;
+  // signs of the three kept weights in position order
+  uint32_t f, g, h;
+  switch (z) {
+    case 0: f = n1; g = n2; h = n3; break;
+    case 1: f = n0; g = n2; h = n3; break;
+    case 2: f = n0; g = n1; h = n3; break;
+    default: f = n0; g = n1; h = n2; break;
+  }
+  const uint32_t p = 4u * (uint32_t)z + 2u * (g ^ f) + (h ^ f);
+  return 2u * p + f;
+}
+
+// One wave per format tile: lane r encodes the 32 blocks of tile row r and
+// writes its 16 + 4 bytes (both stores coalesced across the wave).
+__global__ __launch_bounds__(64) void pack_codes_kernel(const float* __restrict__ W,
+                                                        uint8_t* __restrict__ packed,
+                                                        int N, int K) {
+  const int KT = K / kTileK;
+  const int rt = blockIdx.x / KT, kt = blockIdx.x % KT;
+  const int lane = threadIdx.x;
+  const int n = rt * kTileRows + lane;
+  if (n >= N) return;
+  const float4* src = reinterpret_cast<const float4*>(W + (size_t)n * K + (size_t)kt * kTileK);
+  uint32_t w[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    const float4 v = src[b];
+    const uint32_t c = encode_block(v.x, v.y, v.z, v.w);
+    const int bit = 5 * b, d = bit >> 5, sh = bit & 31;
+    w[d] |= c << sh;
+    if (sh > 27) w[d + 1] |= c >> (32 - sh);
+  }
+  uint8_t* tile = packed + tile_offset(rt, kt, KT);
+  *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint32_t*>(tile + kTileHiOff + 4 * lane) = w[4];
+}
+
+// One thread per row: alpha[n] = sum of kept |w| in ascending k, in double,
+// divided once by the kept count and rounded once to float.
+__global__ __launch_bounds__(256) void pack_alpha_kernel(const float* __restrict__ W,
+                                                         float* __restrict__ alpha, int N,
+                                                         int K) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const float4* src = reinterpret_cast<const float4*>(W + (size_t)n * K);
+  double S = 0.0;
+  for (int b = 0; b < K / 4; ++b) {
+    const float4 v = src[b];
+    const float a[4] = {fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w)};
+    int z = 0;
+    if (a[1] < a[z]) z = 1;
+    if (a[2] < a[z]) z = 2;
+    if (a[3] < a[z]) z = 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j != z) S += (double)a[j];
+  }
+  alpha[n] = (float)(S / (double)(3 * (K / 4)));
+}
+
+// One workgroup per token: s = max|x| / 127, q = clamp(rint(x / s), +-127).
+__global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x,
+                                                           int8_t* __restrict__ q,
+                                                           float* __restrict__ s_x, int K) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)m * K);
+  const int K4 = K / 4;
+  float amax = 0.0f;
+  for (int i = threadIdx.x; i < K4; i += blockDim.x) {
+    const float4 v = xr[i];
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const bool zero = !(amax > 0.0f);
+  const float s = zero ? 1.0f : amax / 127.0f;
+  if (threadIdx.x == 0) s_x[m] = s;
+  char4* qr = reinterpret_cast<char4*>(q + (size_t)m * K);
+  for (int i = threadIdx.x; i < K4; i += blockDim.x) {
+    const float4 v = xr[i];
+    char4 o = make_char4(0, 0, 0, 0);
+    if (!zero) {
+      o.x = (signed char)fminf(fmaxf(rintf(v.x / s), -127.0f), 127.0f);
+      o.y = (signed char)fminf(fmaxf(rintf(v.y / s), -127.0f), 127.0f);
+      o.z = (signed char)fminf(fmaxf(rintf(v.z / s), -127.0f), 127.0f);
+      o.w = (signed char)fminf(fmaxf(rintf(v.w / s), -127.0f), 127.0f);
+    }
+    qr[i] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, float* alpha,
+                                hipStream_t stream) {
+  const int tiles = (N / kTileRows) * (K / kTileK);
+  hipLaunchKernelGGL(pack_codes_kernel, dim3(tiles), dim3(64), 0, stream, W, packed, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_alpha_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, W, alpha,
+                     N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_act(const float* x, int M, int K, int8_t* q, float* s_x,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(quantize_act_kernel, dim3(M), dim3(256), 0, stream, x, q, s_x, K);
+  return hipGetLastError();
+}
+
+}  // namespace sherry

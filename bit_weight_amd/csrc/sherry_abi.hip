@@ -1,0 +1,204 @@
+// C ABI of libsherry: host-side validation, launch planning and dispatch.
+// Every argument error is detected here before any HIP call.
+#include <mutex>
+#include <string.h>
+
+#include "../../include/sherry.h"
+#include "sherry_device.h"
+#include "sherry_launch.h"
+
+namespace sherry {
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device check that the current device is a gfx950, cached.
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+sherry_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SHERRY_ERR_HIP;
+  if (dev >= kMaxDevices) return SHERRY_ERR_DEVICE;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      g_dev_ok[dev] = -1;
+      return;
+    }
+    g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  });
+  if (g_dev_ok[dev] < 0) return SHERRY_ERR_HIP;
+  return g_dev_ok[dev] == 1 ? SHERRY_OK : SHERRY_ERR_DEVICE;
+}
+
+bool shape_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && N >= 1 && K >= 1 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim &&
+         K % kTileK == 0 && N % kTileRows == 0;
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(int M, int N, int K) {
+  GemmPlan p{};
+  if (M > kLutMaxM) {
+    constexpr int BM = 128, BN = 128;
+    p.path = 1;
+    p.grid = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+    p.block = 256;
+    p.splits = 1;
+    p.cpl = K / kTileK;
+    p.groups = 0;
+    p.lds_bytes = (BM + BN) * (kTileK + 16) + 32 * 4;
+    p.ws_bytes = 0;
+    return p;
+  }
+  const int MP = (M + 1) / 2;
+  const int KT = K / kTileK;
+  const int RT = N / kTileRows;
+  const int G = (RT + kGemvWaves - 1) / kGemvWaves;
+  constexpr int kTargetWorkgroups = 1024;
+  int want = (kTargetWorkgroups + G - 1) / G;
+  if (want < 1) want = 1;
+  if (want > KT) want = KT;
+  const int need = (KT + want - 1) / want;  // k-tiles per split
+  int cpl = 1;
+  while (cpl < need && cpl < 8 && (cpl * 2) * MP <= 8) cpl *= 2;  // tables <= 32 KB
+  const int splits = (KT + cpl - 1) / cpl;
+  p.path = 0;
+  p.groups = G;
+  p.cpl = cpl;
+  p.splits = splits;
+  p.grid = G * splits;
+  p.block = kGemvRows;
+  p.lds_bytes = (32 * cpl * MP * 32 + 4) * 4;
+  p.ws_bytes = splits > 1 ? kWsCounterBytes * (((size_t)G * 4 + kWsCounterBytes - 1) / kWsCounterBytes) +
+                                (size_t)G * splits * M * kGemvRows * sizeof(int32_t)
+                          : 0;
+  return p;
+}
+
+}  // namespace sherry
+
+using namespace sherry;
+
+namespace {
+
+sherry_status run_gemm(const int8_t* x, const float* s_x, const void* packed, const float* alpha,
+                       float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!x || !packed || (y && (!s_x || !alpha)) || (!y && !acc)) return SHERRY_ERR_NULL;
+  if (!shape_ok(M, N, K)) return SHERRY_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 16) || (y && !aligned(y, 4)) || (acc && !aligned(acc, 4)) ||
+      (s_x && !aligned(s_x, 4)) || (alpha && !aligned(alpha, 4)))
+    return SHERRY_ERR_ALIGN;
+  const GemmPlan plan = plan_gemm((int)M, (int)N, (int)K);
+  if (plan.ws_bytes > 0) {
+    if (!workspace) return SHERRY_ERR_WORKSPACE;
+    if (workspace_bytes < plan.ws_bytes) return SHERRY_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SHERRY_ERR_ALIGN;
+  }
+  const sherry_status d = check_device();
+  if (d != SHERRY_OK) return d;
+  GemmArgs args{};
+  args.x = x;
+  args.s_x = s_x;
+  args.packed = static_cast<const uint8_t*>(packed);
+  args.alpha = alpha;
+  args.y = y;
+  args.acc = y ? nullptr : acc;
+  args.M = (int)M;
+  args.N = (int)N;
+  args.K = (int)K;
+  if (plan.ws_bytes > 0) {
+    args.counters = static_cast<uint32_t*>(workspace);
+    const size_t cbytes =
+        kWsCounterBytes * (((size_t)plan.groups * 4 + kWsCounterBytes - 1) / kWsCounterBytes);
+    args.partials = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + cbytes);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = plan.path == 0 ? launch_lut_gemv(plan, args, s) : launch_mfma_gemm(plan, args, s);
+  return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sherry_status_string(int status) {
+  switch (status) {
+    case SHERRY_OK: return "SHERRY_OK";
+    case SHERRY_ERR_NULL: return "SHERRY_ERR_NULL: a required pointer is NULL";
+    case SHERRY_ERR_SHAPE: return "SHERRY_ERR_SHAPE: need 1<=M,N,K<=2^20, K%128==0, N%64==0";
+    case SHERRY_ERR_ALIGN: return "SHERRY_ERR_ALIGN: pointer alignment requirement not met";
+    case SHERRY_ERR_WORKSPACE: return "SHERRY_ERR_WORKSPACE: workspace missing or too small";
+    case SHERRY_ERR_HIP: return "SHERRY_ERR_HIP: a HIP call or kernel launch failed";
+    case SHERRY_ERR_DEVICE: return "SHERRY_ERR_DEVICE: current device is not gfx950";
+    default: return "SHERRY_ERR_UNKNOWN";
+  }
+}
+
+size_t sherry_packed_bytes(int64_t N, int64_t K) {
+  if (!shape_ok(1, N, K)) return 0;
+  return (size_t)N * (size_t)K * 5 / 32;
+}
+
+size_t sherry_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!shape_ok(M, N, K)) return 0;
+  return plan_gemm((int)M, (int)N, (int)K).ws_bytes;
+}
+
+sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path, int* grid, int* block,
+                               int* splits, int* lds_bytes) {
+  if (!shape_ok(M, N, K)) return SHERRY_ERR_SHAPE;
+  const GemmPlan p = plan_gemm((int)M, (int)N, (int)K);
+  if (path) *path = p.path;
+  if (grid) *grid = p.grid;
+  if (block) *block = p.block;
+  if (splits) *splits = p.splits;
+  if (lds_bytes) *lds_bytes = p.lds_bytes;
+  return SHERRY_OK;
+}
+
+sherry_status sherry_quantize_pack(const float* W, int64_t N, int64_t K, void* packed, float* alpha,
+                                   void* stream) {
+  if (!W || !packed || !alpha) return SHERRY_ERR_NULL;
+  if (!shape_ok(1, N, K)) return SHERRY_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(alpha, 4)) return SHERRY_ERR_ALIGN;
+  const sherry_status d = check_device();
+  if (d != SHERRY_OK) return d;
+  const hipError_t e = launch_quantize_pack(W, (int)N, (int)K, static_cast<uint8_t*>(packed), alpha,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+}
+
+sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K, int8_t* q, float* s_x,
+                                  void* stream) {
+  if (!x || !q || !s_x) return SHERRY_ERR_NULL;
+  if (M < 1 || K < 4 || M > kMaxDim || K > kMaxDim || K % 4 != 0) return SHERRY_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s_x, 4)) return SHERRY_ERR_ALIGN;
+  const sherry_status d = check_device();
+  if (d != SHERRY_OK) return d;
+  const hipError_t e = launch_quantize_act(x, (int)M, (int)K, q, s_x, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+}
+
+sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed, const float* alpha,
+                          float* y, int64_t M, int64_t N, int64_t K, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!y) return SHERRY_ERR_NULL;
+  return run_gemm(x, s_x, packed, alpha, y, nullptr, M, N, K, workspace, workspace_bytes, stream);
+}
+
+sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc, int64_t M, int64_t N,
+                              int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!acc) return SHERRY_ERR_NULL;
+  return run_gemm(x, nullptr, packed, nullptr, nullptr, acc, M, N, K, workspace, workspace_bytes,
+                  stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Device-side definitions shared by the gfx950 kernels of libsherry.
+//
+// Format (see include/sherry.h): 5-bit code c = 2*p + s per 4-weight block;
+// tiles of 64 rows x 128 columns, 1280 bytes, row-tile-major; a row's 32
+// codes in a tile are a 160-bit little-endian string split 16 + 4 bytes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sherry {
+
+constexpr int kTileRows = 64;     // rows per format tile (one per wave lane)
+constexpr int kTileK = 128;       // weights per row per tile (32 blocks)
+constexpr int kTileBytes = 1280;  // 64 rows * 32 codes * 5 bits / 8
+constexpr int kTileHiOff = 1024;  // byte offset of the 4-byte code parts
+
+// Value (-1, 0 or +1) at position j of the block whose code is c.  The
+// pattern index p = c >> 1 names the zero position z = p >> 2 and whether
+// the 2nd / 3rd nonzero (in position order) flips sign relative to the 1st;
+// the low bit of c negates the whole block.  [Sherry page §2.1]
+__host__ __device__ constexpr int code_value(int c, int j) {
+  const int p = c >> 1, z = p >> 2;
+  if (j == z) return 0;
+  const int rank = j < z ? j : j - 1;  // 0,1,2 = order among the nonzeros
+  const int flip = rank == 0 ? 0 : (rank == 1 ? (p >> 1) & 1 : p & 1);
+  const int v = flip ? -1 : 1;
+  return (c & 1) ? -v : v;
+}
+
+// The block of code c as 4 int8 lanes of a dword (byte j = position j).
+__host__ __device__ constexpr uint32_t code_word(int c) {
+  uint32_t w = 0;
+  for (int j = 0; j < 4; ++j) w |= (uint32_t)(uint8_t)(int8_t)code_value(c, j) << (8 * j);
+  return w;
+}
+
+// 5-bit code j (0..31) of a row's 160-bit string held in w[0..4].  Called
+// with a compile-time j inside unrolled loops, so the branch folds away.
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[5], int j) {
+  const int bit = 5 * j, d = bit >> 5, sh = bit & 31;
+  if (sh <= 27) return (w[d] >> sh) & 31u;
+  return __builtin_amdgcn_alignbit(w[d + 1], w[d], sh) & 31u;
+}
+
+// Byte offset of format tile (rt, kt) for a matrix with K columns.
+__device__ __forceinline__ size_t tile_offset(int rt, int kt, int KT) {
+  return ((size_t)rt * (size_t)KT + (size_t)kt) * (size_t)kTileBytes;
+}
+
+}  // namespace sherry

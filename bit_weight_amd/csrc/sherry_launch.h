@@ -1,0 +1,48 @@
+// Internal launch interface between the C ABI (sherry_abi.hip) and the
+// kernel translation units.  Shapes are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sherry {
+
+// Launch plan of the product for one shape (host-side, pure).
+struct GemmPlan {
+  int path;        // 0 = lookup-table GEMV, 1 = decode + int8 MFMA GEMM
+  int grid;        // workgroups
+  int block;       // threads per workgroup
+  int splits;      // K-splits per row group (GEMV)
+  int cpl;         // format k-tiles per lane per split (GEMV)
+  int groups;      // output row groups (GEMV)
+  int lds_bytes;   // dynamic + static LDS per workgroup
+  size_t ws_bytes; // workspace bytes required
+};
+
+constexpr int kLutMaxM = 16;          // M <= 16 takes the lookup-table path
+constexpr int kGemvWaves = 4;         // waves (64 rows each) per GEMV workgroup
+constexpr int kGemvRows = 64 * kGemvWaves;
+constexpr size_t kWsCounterBytes = 256;  // alignment of the partials area
+
+GemmPlan plan_gemm(int M, int N, int K);
+
+struct GemmArgs {
+  const int8_t* x;
+  const float* s_x;
+  const uint8_t* packed;
+  const float* alpha;
+  float* y;            // fp32 output, or
+  int32_t* acc;        // int32 output (exactly one of y / acc is non-null)
+  int M, N, K;
+  uint32_t* counters;  // workspace: one arrival counter per row group
+  int32_t* partials;   // workspace: per-split int32 partial sums
+};
+
+hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, float* alpha,
+                                hipStream_t stream);
+hipError_t launch_quantize_act(const float* x, int M, int K, int8_t* q, float* s_x,
+                               hipStream_t stream);
+hipError_t launch_lut_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
+hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
+
+}  // namespace sherry

@@ -1,0 +1,136 @@
+/*
+ * sherry.h -- C ABI of the Sherry 3:4-sparse ternary matmul library for
+ * AMD MI355X (gfx950).
+ *
+ * Method: the page "Sherry框架：三元量化与3:4稀疏优化LLM推理"
+ * (pnsm.cn/news/1195499.html).  Weights are ternary {-1,0,+1} with exactly
+ * three nonzeros in every block of four consecutive weights of a row
+ * (§1.1).  A block is stored in 5 bits: a 4-bit index into the 16 canonical
+ * patterns plus one sign bit, 1.25 bit/weight (§2.1).  Inference cuts the
+ * int8 activations into 4-element segments, builds one table of the 16
+ * pattern dot products per segment, looks each weight block up, applies its
+ * sign, sums in integers and rescales once in float (§2.2).  The ternary
+ * block is the solution of min ||W - a*T||^2 with ||T||_0 = 3: keep the three
+ * largest |w| with their signs (§3.1).
+ *
+ * Conventions shared by every entry point
+ *   - W is [N,K] row-major fp32 (N outputs, K inputs); x and y are [M,K] and
+ *     [M,N] row-major.  y[m,n] = sum_k x[m,k] * W[n,k] in the quantized
+ *     domain: y = ((float)acc[m,n] * s_x[m]) * alpha[n],
+ *     acc[m,n] = sum_k q[m,k] * T[n,k] exactly in int32.
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
+ *     The caller allocates and frees every buffer; the library allocates no
+ *     device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on `stream` and returns; results are
+ *     visible after the caller synchronizes the stream.
+ *   - Argument errors are found on the host before any HIP call; such a call
+ *     enqueues nothing and returns a negative status.  A failed launch
+ *     returns SHERRY_ERR_HIP.  A fault inside a kernel is reported by the
+ *     caller's next synchronizing HIP call, not by this library.
+ *   - Shapes supported: K % 128 == 0, N % 64 == 0, 1 <= M,N,K <= 2^20.
+ *   - Code 5-bit layout ("packed"): code c = 2*p + s per block; p = 4*z +
+ *     2*r1 + r2 where z is the zero position and r1 (r2) says the 2nd (3rd)
+ *     nonzero's sign differs from the 1st's; s = 1 iff the 1st nonzero is -1.
+ *     Rows are grouped in tiles of 64 rows x 128 columns (1280 bytes),
+ *     row-tile-major and column-tile-minor.  A row's 32 codes in a tile form
+ *     a 160-bit little-endian string with code j at bits [5j, 5j+5); bits
+ *     0..127 of tile row r sit at tile byte 16*r and bits 128..159 at tile
+ *     byte 1024 + 4*r.  Total sherry_packed_bytes(N,K) = N*K*5/32 bytes.
+ */
+#ifndef SHERRY_H
+#define SHERRY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SHERRY_OK = 0,
+  SHERRY_ERR_NULL = -1,      /* a required pointer is NULL */
+  SHERRY_ERR_SHAPE = -2,     /* M, N or K out of range or not a multiple */
+  SHERRY_ERR_ALIGN = -3,     /* a pointer is not aligned as required */
+  SHERRY_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
+  SHERRY_ERR_HIP = -5,       /* a HIP runtime call or launch failed */
+  SHERRY_ERR_DEVICE = -6     /* the current device is not a gfx950 GPU */
+} sherry_status;
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* sherry_status_string(int status);
+
+/* Bytes of the packed 5-bit weight format for an [N,K] matrix: N*K*5/32.
+ * Host-only, pure; returns 0 for an unsupported shape. */
+size_t sherry_packed_bytes(int64_t N, int64_t K);
+
+/* Bytes of scratch that sherry_gemm / sherry_gemm_i32 need for this shape
+ * (0 when the chosen kernel needs none).  Host-only, pure.
+ * The workspace must be zero-filled once before its first use; every
+ * completed call leaves it ready for the next call (its counters return to
+ * zero), so one zero-filled buffer of the largest size needed can serve any
+ * sequence of calls on one stream.  Calls that run concurrently must not
+ * share a workspace. */
+size_t sherry_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Offline compression (kernel 1), §3.1 and §2.1.
+ *   W      [N,K] fp32, finite values, 16-byte aligned (read only).
+ *   packed sherry_packed_bytes(N,K) bytes, 16-byte aligned (written).
+ *   alpha  [N] fp32 (written): alpha[n] = (sum of the kept |W[n,k]|,
+ *          accumulated in double in ascending k) / (3*K/4), rounded once.
+ * Per block the smallest |w| is dropped (the lowest index on ties) and the
+ * other three keep their signs (w < 0 -> -1, otherwise +1, so -0.0 -> +1). */
+sherry_status sherry_quantize_pack(const float* W, int64_t N, int64_t K,
+                                   void* packed, float* alpha, void* stream);
+
+/* Per-token symmetric int8 quantization of activations (the input stage of
+ * the product; the page's lookup works on int8 segments, §2.2).
+ *   x    [M,K] fp32, finite, 16-byte aligned.  K % 4 == 0 is enough here.
+ *   q    [M,K] int8 (written), 4-byte aligned.
+ *   s_x  [M] fp32 (written): s = max_k |x[m,k]| / 127 (float division);
+ *        q = clamp(rint(x / s), -127, 127) rounding half to even.
+ *        An all-zero row gives s = 1 and q = 0. */
+sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
+                                  int8_t* q, float* s_x, void* stream);
+
+/* The product, §2.2: y[m,n] = ((float)acc[m,n] * s_x[m]) * alpha[n] with
+ * acc[m,n] = sum_k x[m,k] * T[n,k] in int32 (exact; any int8 value of x is
+ * accepted, -128 included).
+ *   x        [M,K] int8, 16-byte aligned.
+ *   s_x      [M] fp32.            alpha  [N] fp32 (from sherry_quantize_pack).
+ *   packed   packed weights, 16-byte aligned.
+ *   y        [M,N] fp32 (written), 4-byte aligned.
+ *   workspace / workspace_bytes: scratch of at least
+ *            sherry_workspace_bytes(M,N,K) bytes, 256-byte aligned, zero
+ *            filled before first use (may be NULL when that size is 0).
+ * M <= 16 runs the lookup-table GEMV (per-segment tables of the 16 pattern
+ * dot products and their negations in LDS, one lookup per weight block);
+ * M > 16 decodes the codes to int8 {-1,0,+1} tiles in LDS and contracts them
+ * on int8 matrix cores.  Both return identical results. */
+sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
+                          const float* alpha, float* y, int64_t M, int64_t N,
+                          int64_t K, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Same product, stopping at the int32 accumulators: acc [M,N] int32
+ * (written, 4-byte aligned).  Same kernels and workspace rules. */
+sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,
+                              int64_t M, int64_t N, int64_t K, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Launch plan sherry_gemm uses for a shape (host-only, pure; for
+ * diagnostics and benchmarks).  Any output pointer may be NULL.
+ *   path: 0 = lookup-table GEMV, 1 = decode + int8 matrix-core GEMM.
+ *   grid: workgroups per launch; block: threads per workgroup;
+ *   splits: K-splits per output row group (1 = none);
+ *   lds_bytes: LDS per workgroup. */
+sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path,
+                               int* grid, int* block, int* splits,
+                               int* lds_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHERRY_H */

@@ -1,0 +1,118 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/sherry.h declares, and rejects bad arguments before any HIP call
+(so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_weight_amd as bw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sherry.h")
+
+OK, NULL, SHAPE, ALIGN, WS = 0, -1, -2, -3, -4
+FAKE = 0x10000        # 64 KiB-aligned dummy device address (never dereferenced)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sherry_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = bw.lib()
+    names = _declared()
+    assert "sherry_gemm" in names and "sherry_quantize_pack" in names
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = bw.lib()
+    for code, name in bw.STATUS.items():
+        assert L.sherry_status_string(code).decode().startswith(name)
+    assert L.sherry_status_string(99).decode() == "SHERRY_ERR_UNKNOWN"
+
+
+def test_packed_bytes():
+    assert bw.packed_bytes(4096, 4096) == 4096 * 4096 * 5 // 32 == 2_621_440
+    assert bw.packed_bytes(28672, 8192) == 36_700_160
+    assert bw.packed_bytes(14336, 4096) == 9_175_040
+    assert bw.packed_bytes(4096, 11008) == 7_045_120
+    assert bw.packed_bytes(256, 256) == 10_240
+    assert bw.packed_bytes(64, 100) == 0          # K % 128 != 0
+    assert bw.packed_bytes(65, 128) == 0          # N % 64 != 0
+
+
+def test_plan_dispatch_rule():
+    for M in (1, 2, 3, 8, 15, 16):
+        assert bw.plan(M, 4096, 4096)["path"] == "lut_gemv"
+    for M in (17, 31, 512):
+        assert bw.plan(M, 4096, 4096)["path"] == "decode_mfma"
+    p = bw.plan(1, 4096, 4096)
+    assert p["block"] == 256 and p["grid"] >= 256
+    # the workspace covers the counters plus every split's partial sums
+    if p["splits"] > 1:
+        assert bw.workspace_bytes(1, 4096, 4096) >= p["grid"] * 256 * 4
+    assert bw.workspace_bytes(512, 14336, 4096) == 0
+
+
+def _gemm(**kw):
+    a = dict(x=FAKE, s=FAKE, p=FAKE, al=FAKE, y=FAKE, M=1, N=64, K=128, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return bw.lib().sherry_gemm(a["x"], a["s"], a["p"], a["al"], a["y"], a["M"], a["N"], a["K"],
+                                a["ws"], a["wsb"], None)
+
+
+def test_gemm_null_pointers():
+    for k in ("x", "s", "p", "al", "y"):
+        assert _gemm(**{k: None}) == NULL, k
+    assert bw.lib().sherry_gemm_i32(FAKE, FAKE, None, 1, 64, 128, FAKE, 1 << 30, None) == NULL
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 64, 128), (1, 0, 128), (1, 64, 0), (1, 64, 100),
+                                   (1, 64, 132), (1, 65, 128), (1, 96, 128), (-1, 64, 128),
+                                   (1, 64, (1 << 20) + 128), (1 << 21, 64, 128)])
+def test_gemm_bad_shapes(M, N, K):
+    assert _gemm(M=M, N=N, K=K) == SHAPE
+
+
+def test_gemm_misaligned():
+    assert _gemm(x=FAKE + 4) == ALIGN
+    assert _gemm(p=FAKE + 8) == ALIGN
+    assert _gemm(y=FAKE + 2) == ALIGN
+    assert _gemm(s=FAKE + 1) == ALIGN
+    assert _gemm(al=FAKE + 2) == ALIGN
+
+
+def test_gemm_workspace_checks():
+    M, N, K = 1, 4096, 4096
+    need = bw.workspace_bytes(M, N, K)
+    assert need > 0
+    assert _gemm(M=M, N=N, K=K, ws=None) == WS
+    assert _gemm(M=M, N=N, K=K, wsb=need - 1) == WS
+    assert _gemm(M=M, N=N, K=K, ws=FAKE + 64) == ALIGN
+
+
+def test_quantize_pack_and_act_validation():
+    L = bw.lib()
+    assert L.sherry_quantize_pack(None, 64, 128, FAKE, FAKE, None) == NULL
+    assert L.sherry_quantize_pack(FAKE, 64, 100, FAKE, FAKE, None) == SHAPE
+    assert L.sherry_quantize_pack(FAKE + 4, 64, 128, FAKE, FAKE, None) == ALIGN
+    assert L.sherry_quantize_pack(FAKE, 64, 128, FAKE + 4, FAKE, None) == ALIGN
+    assert L.sherry_quantize_act(FAKE, 1, 128, None, FAKE, None) == NULL
+    assert L.sherry_quantize_act(FAKE, 0, 128, FAKE, FAKE, None) == SHAPE
+    assert L.sherry_quantize_act(FAKE, 1, 6, FAKE, FAKE, None) == SHAPE
+    assert L.sherry_quantize_act(FAKE + 8, 1, 128, FAKE, FAKE, None) == ALIGN
+
+
+def test_python_wrapper_rejects_cpu_and_noncontiguous():
+    import torch
+    with pytest.raises(RuntimeError):
+        bw.quantize_pack(torch.zeros(64, 128))
+    with pytest.raises(RuntimeError):
+        bw.quantize_act(torch.zeros(1, 128))

@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: packed codes, alpha, q, s_x and the int32 accumulators bit-exact; fp32
+outputs within 1e-5 relative error (the epilogue order is pinned on both
+sides, so they are expected to be bit-identical too).  Each side quantizes
+and packs the same seeded fp32 inputs independently.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_amd as bw
+from bit_weight_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def gpu_pack(W: torch.Tensor):
+    packed, alpha = bw.quantize_pack(W.cuda())
+    torch.cuda.synchronize()
+    return packed, alpha
+
+
+def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray):
+    denom = np.maximum(np.abs(y_ref), np.finfo(np.float32).tiny)
+    rel = np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64)) / denom
+    # exact zeros must stay exact
+    assert np.all((y_ref == 0) <= (y_gpu == 0))
+    assert rel.max() <= RTOL, f"max rel err {rel.max():.3e}"
+
+
+# ---------------------------------------------------------------- packer
+@pytest.mark.parametrize("N,K,std,spikes", [(64, 128, 0.02, False), (256, 256, 0.02, False),
+                                            (192, 384, 0.1, True), (320, 1152, 0.02, False)])
+def test_pack_parity(orc, N, K, std, spikes):
+    _say(f"pack N={N} K={K}")
+    W = synth.weights(N, K, std, spikes, seed=100 + N + K)
+    T, alpha = orc.quantize(W.numpy())
+    packed, galpha = gpu_pack(W)
+    assert np.array_equal(packed.cpu().numpy(), orc.pack(T))
+    assert np.array_equal(galpha.cpu().numpy().view(np.uint32), alpha.view(np.uint32))
+
+
+def test_pack_ties_zeros_and_signed_zero(orc):
+    N, K = 128, 256
+    W = synth.weights(N, K, 1.0, False, seed=7)
+    W = torch.round(W * 2) / 2                 # many equal magnitudes
+    W[0] = 0.0
+    W[1] = -0.0
+    W[2, :4] = torch.tensor([5.0, -5.0, 5.0, -5.0])
+    W[3, 4:8] = torch.tensor([-0.0, 0.0, -1.0, -0.0])
+    W[4] = 5.0 * torch.sign(torch.randn(K, generator=torch.Generator().manual_seed(3)))
+    T, alpha = orc.quantize(W.numpy())
+    packed, galpha = gpu_pack(W)
+    assert np.array_equal(packed.cpu().numpy(), orc.pack(T))
+    assert np.array_equal(galpha.cpu().numpy().view(np.uint32), alpha.view(np.uint32))
+
+
+# ----------------------------------------------------- activation quantizer
+@pytest.mark.parametrize("M,K,outl", [(1, 256, False), (16, 4096, False), (3, 11008, False),
+                                      (512, 4096, True), (2, 4, False)])
+def test_act_quant_parity(orc, M, K, outl):
+    _say(f"act_quant M={M} K={K}")
+    x = synth.activations(M, K, seed=300 + M, outlier_channels=outl)
+    if M >= 3:
+        x[1] = 0.0
+    q, s = orc.act_quant(x.numpy())
+    gq, gs = bw.quantize_act(x.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cpu().numpy(), q)
+    assert np.array_equal(gs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+def test_act_quant_ties_golden(orc):
+    x = torch.tensor([[127.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5, 126.5, -127.0, 0.0, 0.0]])
+    gq, gs = bw.quantize_act(x.cuda())
+    q, s = orc.act_quant(x.numpy())
+    assert gq.cpu().numpy().tolist() == q.tolist()
+    assert gq.cpu().numpy()[0, :10].tolist() == [127, 2, 4, -2, -4, 0, 2, 0, 126, -127]
+    assert float(gs[0]) == 1.0
+
+
+# ----------------------------------------------------- product, edge shapes
+SHAPES = [(64, 128), (192, 384), (320, 1152)]
+MS = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 64, 130]
+
+
+@pytest.fixture(scope="module")
+def packed_cases(orc):
+    out = {}
+    for (N, K) in SHAPES:
+        W = synth.weights(N, K, 0.02, False, seed=500 + N)
+        T, alpha = orc.quantize(W.numpy())
+        packed, galpha = gpu_pack(W)
+        out[(N, K)] = (T, alpha, packed, galpha)
+    return out
+
+
+@pytest.mark.parametrize("M", MS)
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_gemm_edges(orc, packed_cases, M, N, K):
+    _say(f"gemm M={M} N={N} K={K} plan={bw.plan(M, N, K)}")
+    T, alpha, packed, galpha = packed_cases[(N, K)]
+    q = synth.int8_uniform(M, K, seed=700 + M + K)          # includes -128 and 127
+    s_x = (torch.rand(M, generator=torch.Generator().manual_seed(M)) * 0.05 + 0.001).float()
+    acc, y = orc.gemm(q.numpy(), s_x.numpy(), T, alpha)
+    gacc = bw.gemm_i32(q.cuda(), packed, N, K)
+    gy = bw.gemm(q.cuda(), s_x.cuda(), packed, galpha, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(gacc.cpu().numpy(), acc)
+    assert_y_close(gy.cpu().numpy(), y)
+
+
+def test_gemm_extreme_activations(orc, packed_cases):
+    N, K = 192, 384
+    T, alpha, packed, galpha = packed_cases[(N, K)]
+    for M in (1, 4, 16, 40):
+        for fill in (127, -128, 0):
+            q = torch.full((M, K), fill, dtype=torch.int8)
+            acc = orc.gemm_i32(q.numpy(), T)
+            gacc = bw.gemm_i32(q.cuda(), packed, N, K)
+            torch.cuda.synchronize()
+            assert np.array_equal(gacc.cpu().numpy(), acc), (M, fill)
+
+
+def test_gemm_deterministic_and_workspace_reuse(orc, packed_cases):
+    outs = []
+    for (N, K) in SHAPES + SHAPES:
+        T, alpha, packed, galpha = packed_cases[(N, K)]
+        q = synth.int8_uniform(1, K, seed=11)
+        outs.append(bw.gemm_i32(q.cuda(), packed, N, K).cpu().numpy())
+    for a, b in zip(outs[:3], outs[3:]):
+        assert np.array_equal(a, b)
+
+
+# ------------------------------------------------- the workloads, full size
+def _workload_check(orc, name, sample_rows=None):
+    w = synth.WORKLOADS[name]
+    _say(f"workload {w.description}")
+    W = synth.workload_weights(w)
+    x = synth.workload_activations(w)
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    packed, galpha = gpu_pack(W)
+    assert np.array_equal(packed.cpu().numpy(), orc.pack(T)), "packed codes"
+    assert np.array_equal(galpha.cpu().numpy().view(np.uint32), alpha.view(np.uint32)), "alpha"
+    del W
+    gq, gs = bw.quantize_act(x.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cpu().numpy(), q), "q"
+    assert np.array_equal(gs.cpu().numpy().view(np.uint32), s.view(np.uint32)), "s_x"
+    gacc = bw.gemm_i32(gq, packed, w.N, w.K).cpu().numpy()
+    gy = bw.gemm(gq, gs, packed, galpha, w.N, w.K).cpu().numpy()
+    if sample_rows is None:
+        acc, y = orc.gemm(q, s, T, alpha)
+        assert np.array_equal(gacc, acc), "acc"
+        assert_y_close(gy, y)
+    else:
+        rows = sample_rows
+        acc = orc.gemm_i32(q, np.ascontiguousarray(T[rows]))
+        y = orc.epilogue(acc, s, np.ascontiguousarray(alpha[rows]))
+        assert np.array_equal(gacc[:, rows], acc), "acc (sampled)"
+        assert_y_close(np.ascontiguousarray(gy[:, rows]), y)
+
+
+@pytest.mark.parametrize("name", ["1", "2a", "2b", "2c", "3a", "3b", "4"])
+def test_workload_parity(orc, name):
+    _workload_check(orc, name)
+
+
+def test_workload_5_prefill_sampled(orc):
+    w = synth.WORKLOADS["5"]
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N - 1],
+                                     rng.choice(w.N, 251, replace=False)]))
+    _workload_check(orc, "5", sample_rows=rows)
