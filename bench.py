@@ -1,0 +1,319 @@
+"""Benchmark of the Sherry 3:4 ternary matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2a]
+
+A step is one pass of the hot path over one batch of synthetic input:
+per-token int8 quantization of the activations (sherry_quantize_act) and the
+product with the packed weights (sherry_gemm).  Offline packing
+(sherry_quantize_pack) is timed separately and reported under "offline".
+Steps rotate over R copies of the packed weights whose total size exceeds
+twice the 256 MB last-level cache, so every step streams its weights from
+HBM; the K timed steps are captured once into a HIP graph and replayed, with
+HIP events (recorded on the stream the kernels run on) around the replay.
+
+Prints ONE JSON line.  `value` is packed-weight GB/s of the whole step
+(N*K*5/32 bytes per step / step time) on the default workload (decode GEMV,
+LLaMA-7B attention projection: M=1, K=4096, N=4096).  "roofline" is the
+dominant kernel (the LUT-GEMV) against the 8 TB/s HBM peak; "prefill" holds
+the M=512 decode + int8 MFMA product against the 5.0 POP/s int8 peak;
+"workloads" holds every workload's kernel time.  "cpu_baseline" times the CPU
+oracle (single thread) on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+MALL_BYTES = 256 << 20         # last-level (Infinity) cache
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "packed-weight GB/s (% HBM peak) for decode GEMV; int8 TOPS (% MFMA) prefill"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="2a")
+    ap.add_argument("--copies", type=int, default=0, help="rotating weight copies (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="only the default workload")
+    ap.add_argument("--only", default="", help="profile mode: run only these workloads' "
+                    "product launches (comma list), print timings, no JSON contract line")
+    return ap.parse_args()
+
+
+def copies_for(packed_bytes: int, requested: int) -> int:
+    if requested > 0:
+        return requested
+    return max(2, math.ceil(2 * MALL_BYTES / packed_bytes) + 1)
+
+
+class Setup:
+    """Packed weight copies, activations and outputs for one workload, on the GPU."""
+
+    def __init__(self, torch, bw, synth, name: str, copies: int):
+        w = synth.WORKLOADS[name]
+        self.w = w
+        W = synth.workload_weights(w).cuda()
+        x = synth.workload_activations(w)
+        t0 = time.perf_counter()
+        packed, alpha = bw.quantize_pack(W)
+        torch.cuda.synchronize()
+        self.pack_s = time.perf_counter() - t0          # includes first-call setup
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bw.quantize_pack(W)
+        e1.record()
+        torch.cuda.synchronize()
+        self.pack_ms = e0.elapsed_time(e1)
+        del W
+        self.R = copies_for(w.packed_bytes, copies)
+        self.packed = [packed] + [packed.clone() for _ in range(self.R - 1)]
+        self.alpha = [alpha] + [alpha.clone() for _ in range(self.R - 1)]
+        self.x = x.cuda()
+        self.q, self.s = bw.quantize_act(self.x)
+        self.y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        self.ws = torch.zeros(max(bw.workspace_bytes(w.M, w.N, w.K), 256), dtype=torch.uint8,
+                              device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, bw, i: int):
+        q, s = bw.quantize_act(self.x)
+        return self.gemm(bw, i, q, s)
+
+    def gemm(self, bw, i: int, q=None, s=None):
+        r = i % self.R
+        return bw.gemm(self.q if q is None else q, self.s if s is None else s, self.packed[r],
+                       self.alpha[r], self.w.N, self.w.K, out=self.y, workspace=self.ws)
+
+
+def graph_time(torch, fn, n: int, reps: int = 1):
+    """Capture n calls of fn(i) into one graph; return (ms per call, graph)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()                       # first replay uploads the graph (untimed)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        best = ms if best is None else min(best, ms)
+    return best, g
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes a product launch must move at least: packed codes, alpha, int8 x,
+    s_x and the fp32 y."""
+    return w.packed_bytes + 4 * w.N + w.M * w.K + 4 * w.M + 4 * w.M * w.N
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("lut_gemv.hip", "mfma_gemm.hip", "sherry_device.h", "sherry_abi.hip"):
+        with open(os.path.join(ROOT, "bit_weight_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_tag: str):
+    """HBM bytes per launch measured with rocprofv3 counters, read from the
+    committed summary under profiles/; None if absent or if the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha") != kernel_sources_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(name: str, seconds: float):
+    """The CPU oracle (single-threaded C, as it stands) on the same workload:
+    per-token quantization + dense int8 x ternary product + epilogue, repeated
+    for a bounded number of whole steps."""
+    import numpy as np
+    import oracle
+    from bit_weight_amd import synth
+    w = synth.WORKLOADS[name]
+    T, alpha = oracle.quantize(synth.workload_weights(w).numpy())
+    x = synth.workload_activations(w).numpy()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        q, s = oracle.act_quant(x)
+        oracle.gemm(q, s, T, alpha)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 100000:
+            break
+    per = el / n
+    return {"value": round(w.packed_bytes / per / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"workload {name} (M={w.M}, K={w.K}, N={w.N}): {n} whole steps "
+                      f"(act quant + dense int8 x unpacked-ternary product + epilogue) in "
+                      f"{el:.1f} s, {per * 1e3:.2f} ms/step; host {platform.processor() or platform.machine()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_weight_amd as bw
+    from bit_weight_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    bw.lib()
+
+    if args.only:
+        # a plain device copy of known size, for scaling HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        for name in args.only.split(","):
+            st = Setup(torch, bw, synth, name, args.copies)
+            n = max(args.steps, st.R)
+            ms, _ = graph_time(torch, lambda i: st.gemm(bw, i), n)
+            print(f"{name}: {ms * 1e3:.3f} us/launch, {st.w.packed_bytes / ms / 1e6:.1f} GB/s packed,"
+                  f" R={st.R}, plan={bw.plan(st.w.M, st.w.N, st.w.K)}", flush=True)
+            del st
+            torch.cuda.empty_cache()
+        return
+
+    name = args.workload
+    st = Setup(torch, bw, synth, name, args.copies)
+    w = st.w
+    # correctness of graph replay against eager (replayed several times)
+    ref = st.step(bw, 0).clone()
+    torch.cuda.synchronize()
+    # warmup steps, then the timed steps
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for i in range(args.warmup):
+            st.step(bw, i)
+    gw.replay()
+    torch.cuda.synchronize()
+    gt = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gt):
+        for i in range(args.steps):
+            st.step(bw, i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    gt.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.steps
+    ok = bool(torch.equal(st.y, ref))
+    st.step(bw, 1)                  # eager work between replays
+    torch.cuda.synchronize()
+    gt.replay()
+    torch.cuda.synchronize()
+    ok = ok and bool(torch.equal(st.y, ref))
+
+    # dominant kernel alone: back-to-back products over the rotating copies
+    n_k = max(args.steps, st.R)
+    gemm_ms, _ = graph_time(torch, lambda i: st.gemm(bw, i), n_k, reps=3)
+    act_ms, _ = graph_time(torch, lambda i: bw.quantize_act(st.x), n_k, reps=3)
+    alg = algorithmic_bytes(w)
+    achieved = alg / gemm_ms / 1e6
+    traffic = traffic_from_profile(f"lut_gemv_{name}")
+    value = w.packed_bytes / step_ms / 1e6
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV, LLaMA-7B attention projection (3:4 ternary W, "
+                               "per-token int8 x)",
+                   "M": w.M, "K": w.K, "N": w.N, "weights": f"Normal(0,{w.w_std})",
+                   "rotating_copies": st.R, "step": "sherry_quantize_act + sherry_gemm",
+                   "plan": bw.plan(w.M, w.N, w.K), "parallelism": "none (1 GPU)"},
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "lut_gemv_kernel",
+                     "kernel_us": round(gemm_ms * 1e3, 3), "bytes_per_launch": alg,
+                     "packed_bytes_per_launch": w.packed_bytes},
+        "kernels_us": {"sherry_gemm": round(gemm_ms * 1e3, 3),
+                       "sherry_quantize_act": round(act_ms * 1e3, 3)},
+        "graph_replay_matches_eager": ok,
+        "offline": {"sherry_quantize_pack_ms": round(st.pack_ms, 3),
+                    "pack_input_GB_s": round(4 * w.N * w.K / st.pack_ms / 1e6, 1)},
+    }
+    del st
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        wl = {}
+        for nm in ("1", "2a", "2b", "2c", "3a", "3b", "4", "5"):
+            s2 = Setup(torch, bw, synth, nm, 0)
+            ms, _ = graph_time(torch, lambda i: s2.gemm(bw, i), max(200, s2.R), reps=3)
+            ww = s2.w
+            ent = {"M": ww.M, "K": ww.K, "N": ww.N, "kernel_us": round(ms * 1e3, 3),
+                   "plan": bw.plan(ww.M, ww.N, ww.K), "rotating_copies": s2.R}
+            if ww.M > 16:
+                tops = 2.0 * ww.M * ww.N * ww.K / ms / 1e9
+                ent.update({"TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
+            else:
+                gbs = ww.packed_bytes / ms / 1e6
+                ent.update({"packed_GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+            wl[nm] = ent
+            del s2
+            torch.cuda.empty_cache()
+        out["workloads"] = wl
+        p5 = wl["5"]
+        out["prefill"] = {"workload": "prefill GEMM M=512 K=4096 N=14336",
+                          "value": p5["TOPS"], "unit": "TOPS",
+                          "roofline": {"bound": "mfma", "achieved": p5["TOPS"],
+                                       "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                                       "frac": p5["mfma_frac"], "traffic": None,
+                                       "kernel": "mfma_gemm_kernel"}}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ import threading
 import torch
 
 __all__ = [
-    "SherryError", "lib", "packed_bytes", "workspace_bytes", "plan",
+    "SherryError", "lib", "packed_bytes", "workspace_bytes", "plan", "plan_override",
     "quantize_pack", "quantize_act", "gemm", "gemm_i32", "linear",
 ]
 
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
                 "sherry_packed_bytes": ([i64, i64], sz),
                 "sherry_workspace_bytes": ([i64, i64, i64], sz),
                 "sherry_gemm_plan": ([i64, i64, i64, ip, ip, ip, ip, ip], ci),
+                "sherry_gemm_plan_override": ([ci, ci, ci], ci),
                 "sherry_quantize_pack": ([vp, i64, i64, vp, vp, vp], ci),
                 "sherry_quantize_act": ([vp, i64, i64, vp, vp, vp], ci),
                 "sherry_gemm": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
@@ -118,6 +119,11 @@ def plan(M: int, N: int, K: int) -> dict:
     path, grid, block, splits, lds = (v.value for v in vals)
     return {"path": "lut_gemv" if path == 0 else "decode_mfma", "grid": grid,
             "block": block, "splits": splits, "lds_bytes": lds}
+
+
+def plan_override(rw: int = 0, ch: int = 0, splits: int = 0) -> None:
+    """Tuning knob: force the LUT-GEMV launch plan (0 = built-in choice)."""
+    _check(lib().sherry_gemm_plan_override(rw, ch, splits), "sherry_gemm_plan_override")
 
 
 def quantize_pack(W: torch.Tensor):

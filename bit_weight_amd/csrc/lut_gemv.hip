@@ -6,21 +6,28 @@
 // results are summed in integers, with one float rescale at the end.
 //
 // Mapping on gfx950 (wave64):
-//  * A workgroup owns 4 format row tiles (256 output rows, one row per lane)
-//    and a contiguous range of `cpl` format k-tiles (128 inputs each).
-//  * Each lane first issues its code loads (16 + 4 bytes per k-tile, both
-//    coalesced across the wave), then the workgroup builds the tables for
-//    its k-range while those loads are in flight.
+//  * A workgroup has RW x KW waves: RW format row tiles (64 output rows each,
+//    one row per lane) times KW waves that share a row tile and take turns
+//    over its k-tiles.  It covers the k-tiles of one K-split in stages of CH
+//    k-tiles (128 inputs each); the tables of one stage live in LDS.
+//  * Each lane streams its codes, 16 + 4 bytes per k-tile, both loads
+//    coalesced across the wave; the next stage's codes are requested before
+//    the current stage's lookups.
 //  * Table layout: dword [segment][token pair][code], 32 codes per table
 //    (128 bytes).  Entry 2p holds the pattern-p dot products of two tokens as
 //    two int16 halves; entry 2p+1 holds their negations, so the code's sign
 //    bit is applied by the table half it selects.  All lanes of a wave read
-//    the same 128-byte table at a time, so the read is bank-conflict free.
-//  * Lookups accumulate two tokens per v_pk_add_u16 in int16 halves, which
-//    are widened into int32 after every k-tile (32 codes, |sum| <= 32*384).
-//  * K-splits of one row group publish int32 partial sums; the last
-//    workgroup to arrive (an agent-scope counter) adds them in split order
-//    and writes the output, then resets the counter for the next call.
+//    the same 128-byte table at a time, so a lookup is bank-conflict free.
+//    One thread builds the four patterns that share a zero position with
+//    packed 16-bit adds: (a+b)+-c and (a-b)+-c.
+//  * Lookups accumulate two tokens per v_pk_add_u16 in int16 halves, widened
+//    into int32 after every k-tile (32 codes, |sum| <= 32*384 < 2^15).
+//  * Waves sharing a row tile add their sums through LDS.  K-splits of one
+//    row group then add theirs into a zero-filled 64-bit accumulator per
+//    output with one returning atomic, 2^32 + partial: the high word counts
+//    arrivals, the low word is the exact int32 sum.  The split that brings
+//    the count to `splits` writes the output and stores the zero back, so
+//    the reduction costs one memory round trip and no cache maintenance.
 #include "sherry_device.h"
 #include "sherry_launch.h"
 
@@ -29,160 +36,193 @@ namespace {
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
 
-template <int MP, int CPL>
-__global__ __launch_bounds__(kGemvRows) void lut_gemv_kernel(GemmArgs a, int splits) {
-  // [32*CPL segments][MP pairs][32 codes], then one flag dword.  Nothing
-  // else lives in LDS, so the tables start at address 0 and every lookup's
-  // segment offset folds into the ds_read immediate.
-  extern __shared__ uint32_t lut[];
-  constexpr int kLutDwords = 32 * CPL * MP * 32;
-  int& is_last = *reinterpret_cast<int*>(&lut[kLutDwords]);
+__device__ __forceinline__ short2_t pair_of(int x0, int x1, int j) {
+  // int8 activation j of two tokens' segment words, widened to int16 halves
+  return short2_t{(short)(int8_t)(x0 >> (8 * j)), (short)(int8_t)(x1 >> (8 * j))};
+}
+
+template <int MP, int CH, int RW, int KW>
+__global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int splits,
+                                                                 int kt_per_split) {
+  constexpr int NT = 64 * RW * KW;
+  constexpr int CPW = (CH + KW - 1) / KW;        // k-tiles per wave per stage
+  extern __shared__ uint32_t lut[];               // tables start at LDS 0
 
   const int M = a.M, N = a.N, K = a.K;
-  const int KT = K / kTileK;
+  const int KT = K / kTileK, RT = N / kTileRows;
   const int g = blockIdx.x / splits;
   const int s = blockIdx.x - g * splits;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rt = g * kGemvWaves + wave;
-  const bool active = rt < N / kTileRows;
-  const int kt0 = s * CPL;
-  const int nch = min(CPL, KT - kt0);
+  const int r = wave % RW, q = wave / RW;
+  const int rt = g * RW + r;
+  const bool active = rt < RT;
+  const int kt_begin = s * kt_per_split;
+  const int kt_end = min(KT, kt_begin + kt_per_split);
+  const int nst = (kt_end - kt_begin + CH - 1) / CH;
 
-  // 1. stream this lane's codes (issued first; consumed after the table build)
-  uint32_t w[CPL][5];
+  auto load_stage = [&](int st, uint32_t (&w)[CPW][5]) {
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    if (active && c < nch) {
-      const uint8_t* tb = a.packed + tile_offset(rt, kt0 + c, KT);
-      const uint4 lo = *reinterpret_cast<const uint4*>(tb + 16 * lane);
-      w[c][0] = lo.x; w[c][1] = lo.y; w[c][2] = lo.z; w[c][3] = lo.w;
-      w[c][4] = *reinterpret_cast<const uint32_t*>(tb + kTileHiOff + 4 * lane);
-    } else {
+    for (int i = 0; i < CPW; ++i) {
+      const int c = q + KW * i;
+      const int kt = kt_begin + st * CH + c;
+      if (active && c < CH && kt < kt_end) {
+        const uint8_t* tb = a.packed + tile_offset(rt, kt, KT);
+        const uint4 lo = *reinterpret_cast<const uint4*>(tb + 16 * lane);
+        w[i][0] = lo.x; w[i][1] = lo.y; w[i][2] = lo.z; w[i][3] = lo.w;
+        w[i][4] = *reinterpret_cast<const uint32_t*>(tb + kTileHiOff + 4 * lane);
+      } else {
 #pragma unroll
-      for (int d = 0; d < 5; ++d) w[c][d] = 0;
+        for (int d = 0; d < 5; ++d) w[i][d] = 0;
+      }
     }
-  }
+  };
 
-  // 2. tables: item = (segment, pair, pattern p), p fastest
-  {
-    const int p = threadIdx.x & 15;
-    const uint32_t pw = code_word(2 * p);
-    const int items = 32 * nch * MP * 16;
-    const int kbase = kt0 * kTileK;
-    for (int it = threadIdx.x; it < items; it += kGemvRows) {
-      const int rest = it >> 4;  // segment * MP + pair
-      const int pair = rest % MP;
-      const int seg = rest / MP;
-      const int k = kbase + 4 * seg;
-      const int m0 = 2 * pair, m1 = 2 * pair + 1;
-      const int x0 = m0 < M ? *reinterpret_cast<const int*>(a.x + (size_t)m0 * K + k) : 0;
-      const int x1 = m1 < M ? *reinterpret_cast<const int*>(a.x + (size_t)m1 * K + k) : 0;
-      const int L0 = __builtin_amdgcn_sdot4((int)pw, x0, 0, false);
-      const int L1 = __builtin_amdgcn_sdot4((int)pw, x1, 0, false);
-      const uint32_t pos = ((uint32_t)L0 & 0xFFFFu) | ((uint32_t)L1 << 16);
-      const uint32_t neg = ((uint32_t)(-L0) & 0xFFFFu) | ((uint32_t)(-L1) << 16);
-      *reinterpret_cast<uint2*>(&lut[rest * 32 + 2 * p]) = make_uint2(pos, neg);
-    }
-  }
-  __syncthreads();
+  uint32_t cur[CPW][5];
+  load_stage(0, cur);
 
-  // 3. lookups
   int acc[2 * MP];
 #pragma unroll
   for (int m = 0; m < 2 * MP; ++m) acc[m] = 0;
-  if (active) {
+
+  for (int st = 0; st < nst; ++st) {
+    const int kt_s = kt_begin + st * CH;
+    const int nch = min(CH, kt_end - kt_s);
+    if (st > 0) __syncthreads();  // previous stage's lookups are done
+
+    // tables of this stage: item = (segment, pair, zero position z)
+    {
+      const int items = nch * 32 * MP * 4;
+      for (int it = threadIdx.x; it < items; it += NT) {
+        const int z = it & 3;
+        const int rest = it >> 2;       // segment * MP + pair
+        const int pair = rest % MP;
+        const int seg = rest / MP;
+        const int k = kt_s * kTileK + 4 * seg;
+        const int m0 = 2 * pair, m1 = 2 * pair + 1;
+        const int x0 = m0 < M ? *reinterpret_cast<const int*>(a.x + (size_t)m0 * K + k) : 0;
+        const int x1 = m1 < M ? *reinterpret_cast<const int*>(a.x + (size_t)m1 * K + k) : 0;
+        // the three kept positions in order: ja < jb < jc, none equal to z
+        const int ja = z == 0 ? 1 : 0;
+        const int jb = z <= 1 ? 2 : 1;
+        const int jc = z <= 2 ? 3 : 2;
+        const short2_t ya = pair_of(x0, x1, ja), yb = pair_of(x0, x1, jb),
+                       yc = pair_of(x0, x1, jc);
+        const short2_t t = ya + yb, u = ya - yb;
+        const short2_t zero{0, 0};
+        // pattern 4z + 2*r1 + r2 -> codes 2p (positive) and 2p+1 (negated)
+        const short2_t p0 = t + yc, p1 = t - yc, p2 = u + yc, p3 = u - yc;
+        uint4* dst = reinterpret_cast<uint4*>(&lut[rest * 32 + 8 * z]);
+        dst[0] = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, zero - p0),
+                            __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, zero - p1));
+        dst[1] = make_uint4(__builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, zero - p2),
+                            __builtin_bit_cast(uint32_t, p3), __builtin_bit_cast(uint32_t, zero - p3));
+      }
+    }
+    __syncthreads();
+
+    uint32_t nxt[CPW][5];
+    if (st + 1 < nst) load_stage(st + 1, nxt);
+
+    if (active) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      if (c < nch) {
-        short2_t h[MP];
+      for (int i = 0; i < CPW; ++i) {
+        const int c = q + KW * i;
+        if (c < nch) {
+          short2_t h[MP];
 #pragma unroll
-        for (int i = 0; i < MP; ++i) h[i] = short2_t{0, 0};
-        const uint32_t* lc = lut + c * 32 * MP * 32;
+          for (int pp = 0; pp < MP; ++pp) h[pp] = short2_t{0, 0};
+          const uint32_t* lc = lut + c * (32 * MP * 32);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const uint32_t code = code_at(w[c], j);
+          for (int j = 0; j < 32; ++j) {
+            const uint32_t code = code_at(cur[i], j);
 #pragma unroll
-          for (int i = 0; i < MP; ++i) {
-            const uint32_t v = lc[(j * MP + i) * 32 + code];
-            h[i] += __builtin_bit_cast(short2_t, v);
+            for (int pp = 0; pp < MP; ++pp)
+              h[pp] += __builtin_bit_cast(short2_t, lc[(j * MP + pp) * 32 + code]);
+          }
+#pragma unroll
+          for (int pp = 0; pp < MP; ++pp) {
+            acc[2 * pp] += (int)h[pp].x;
+            acc[2 * pp + 1] += (int)h[pp].y;
           }
         }
-#pragma unroll
-        for (int i = 0; i < MP; ++i) {
-          acc[2 * i] += (int)h[i].x;
-          acc[2 * i + 1] += (int)h[i].y;
-        }
       }
+    }
+    if (st + 1 < nst) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int d = 0; d < 5; ++d) cur[i][d] = nxt[i][d];
     }
   }
 
-  const int n = rt * kTileRows + lane;
-  if (splits > 1) {
-    // 4. publish this split's partial sums; the last arrival reduces
-    int32_t* part = a.partials + ((size_t)g * splits + s) * (size_t)M * kGemvRows;
-    if (active) {
+  // waves that share a row tile: add through LDS into the q == 0 wave
+  if constexpr (KW > 1) {
+    __syncthreads();  // tables no longer needed
+    int* red = reinterpret_cast<int*>(lut);   // [KW-1][2MP][RW*64]
+    if (q > 0) {
 #pragma unroll
       for (int m = 0; m < 2 * MP; ++m)
-        if (m < M) part[(size_t)m * kGemvRows + threadIdx.x] = acc[m];
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(&a.counters[g], 1u, __ATOMIC_ACQ_REL,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-      is_last = (old == (uint32_t)(splits - 1));
+        red[((q - 1) * 2 * MP + m) * (RW * 64) + r * 64 + lane] = acc[m];
     }
     __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    if (active) {
-      const int32_t* base = a.partials + (size_t)g * splits * (size_t)M * kGemvRows;
+    if (q > 0) return;
 #pragma unroll
-      for (int m = 0; m < 2 * MP; ++m) {
-        if (m < M) {
-          int t = 0;
-          for (int s2 = 0; s2 < splits; ++s2)
-            t += base[((size_t)s2 * M + m) * kGemvRows + threadIdx.x];
-          acc[m] = t;
-        }
-      }
-    }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&a.counters[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int qq = 1; qq < KW; ++qq)
+#pragma unroll
+      for (int m = 0; m < 2 * MP; ++m)
+        acc[m] += red[((qq - 1) * 2 * MP + m) * (RW * 64) + r * 64 + lane];
   }
 
-  // 5. epilogue: y = ((float)acc * s_x[m]) * alpha[n]
   if (!active) return;
-  if (a.y) {
-    const float al = a.alpha[n];
+  const int n = rt * kTileRows + lane;
+  const float al = a.y ? a.alpha[n] : 0.0f;
 #pragma unroll
-    for (int m = 0; m < 2 * MP; ++m)
-      if (m < M) {
-        const float t = (float)acc[m] * a.s_x[m];
-        a.y[(size_t)m * N + n] = t * al;
-      }
-  } else {
-#pragma unroll
-    for (int m = 0; m < 2 * MP; ++m)
-      if (m < M) a.acc[(size_t)m * N + n] = acc[m];
+  for (int m = 0; m < 2 * MP; ++m) {
+    if (m >= M) continue;
+    int total = acc[m];
+    if (splits > 1) {
+      unsigned long long* cell = reinterpret_cast<unsigned long long*>(a.partials) + (size_t)m * N + n;
+      const unsigned long long inc = (1ull << 32) + (unsigned long long)(long long)acc[m];
+      const unsigned long long now =
+          __hip_atomic_fetch_add(cell, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+      total = (int)(uint32_t)now;
+      const long long count = ((long long)now - (long long)total) >> 32;
+      if (count != splits) continue;
+      __hip_atomic_store(cell, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (a.y) {
+      const float t = (float)total * a.s_x[m];
+      a.y[(size_t)m * N + n] = t * al;
+    } else {
+      a.acc[(size_t)m * N + n] = total;
+    }
   }
 }
 
-template <int MP, int CPL>
-hipError_t launch_mp_cpl(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  const size_t lds = ((size_t)32 * CPL * MP * 32 + 4) * sizeof(uint32_t);
-  hipLaunchKernelGGL((lut_gemv_kernel<MP, CPL>), dim3(p.grid), dim3(kGemvRows), lds, stream, a,
-                     p.splits);
+template <int MP, int CH, int RW, int KW>
+hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((lut_gemv_kernel<MP, CH, RW, KW>), dim3(p.grid), dim3(64 * RW * KW),
+                     p.lds_bytes, stream, a, p.splits, p.kt_per_split);
   return hipGetLastError();
+}
+
+template <int MP, int CH>
+hipError_t launch_ch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  switch (p.rw) {
+    case 4: return launch_cfg<MP, CH, 4, 1>(p, a, stream);
+    case 2: return launch_cfg<MP, CH, 2, 2>(p, a, stream);
+    case 1: return launch_cfg<MP, CH, 1, 4>(p, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int MP>
 hipError_t launch_mp(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  switch (p.cpl) {
-    case 1: return launch_mp_cpl<MP, 1>(p, a, stream);
-    case 2: return launch_mp_cpl<MP, 2>(p, a, stream);
-    case 4: if constexpr (MP <= 2) return launch_mp_cpl<MP, 4>(p, a, stream); break;
-    case 8: if constexpr (MP <= 1) return launch_mp_cpl<MP, 8>(p, a, stream); break;
+  switch (p.ch) {
+    case 1: return launch_ch<MP, 1>(p, a, stream);
+    case 2: return launch_ch<MP, 2>(p, a, stream);
+    case 4: if constexpr (MP <= 4) return launch_ch<MP, 4>(p, a, stream); break;
+    case 8: if constexpr (MP <= 2) return launch_ch<MP, 8>(p, a, stream); break;
     default: break;
   }
   return hipErrorInvalidValue;

@@ -1,5 +1,6 @@
 // C ABI of libsherry: host-side validation, launch planning and dispatch.
 // Every argument error is detected here before any HIP call.
+#include <atomic>
 #include <mutex>
 #include <string.h>
 
@@ -43,6 +44,16 @@ bool shape_ok(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
+namespace {
+std::atomic<int> g_ovr_rw{0}, g_ovr_ch{0}, g_ovr_splits{0};
+}
+
+void set_plan_override(int rw, int ch, int splits) {
+  g_ovr_rw = rw;
+  g_ovr_ch = ch;
+  g_ovr_splits = splits;
+}
+
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   if (M > kLutMaxM) {
@@ -51,8 +62,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
     p.grid = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     p.block = 256;
     p.splits = 1;
-    p.cpl = K / kTileK;
-    p.groups = 0;
+    p.kt_per_split = K / kTileK;
     p.lds_bytes = (BM + BN) * (kTileK + 16) + 32 * 4;
     p.ws_bytes = 0;
     return p;
@@ -60,25 +70,35 @@ GemmPlan plan_gemm(int M, int N, int K) {
   const int MP = (M + 1) / 2;
   const int KT = K / kTileK;
   const int RT = N / kTileRows;
-  const int G = (RT + kGemvWaves - 1) / kGemvWaves;
-  constexpr int kTargetWorkgroups = 1024;
-  int want = (kTargetWorkgroups + G - 1) / G;
-  if (want < 1) want = 1;
-  if (want > KT) want = KT;
-  const int need = (KT + want - 1) / want;  // k-tiles per split
-  int cpl = 1;
-  while (cpl < need && cpl < 8 && (cpl * 2) * MP <= 8) cpl *= 2;  // tables <= 32 KB
-  const int splits = (KT + cpl - 1) / cpl;
+  int ch_max = 1;                       // one stage of tables stays <= 32 KB
+  while (ch_max < 8 && (ch_max * 2) * MP <= 8) ch_max *= 2;
+
+  int rw = g_ovr_rw.load() > 0 ? g_ovr_rw.load() : 4;
+  if (rw != 1 && rw != 2 && rw != 4) rw = 4;
+  const int G = (RT + rw - 1) / rw;
+  constexpr int kTargetWorkgroups = 512;
+  int splits = g_ovr_splits.load() > 0 ? g_ovr_splits.load() : (kTargetWorkgroups + G - 1) / G;
+  if (splits > KT) splits = KT;
+  if (splits < 1) splits = 1;
+  const int kt_per_split = (KT + splits - 1) / splits;
+  splits = (KT + kt_per_split - 1) / kt_per_split;
+  int ch = 1;
+  const int ch_cap = g_ovr_ch.load() > 0 ? g_ovr_ch.load() : ch_max;
+  while (ch * 2 <= ch_cap && ch * 2 <= ch_max && ch * 2 <= kt_per_split) ch *= 2;
+
+  const int kw = kGemvWaves / rw;
+  const int lut_bytes = ch * 32 * MP * 32 * 4;
+  const int red_bytes = (kw - 1) * 2 * MP * rw * 64 * 4;
   p.path = 0;
   p.groups = G;
-  p.cpl = cpl;
+  p.rw = rw;
+  p.ch = ch;
   p.splits = splits;
+  p.kt_per_split = kt_per_split;
   p.grid = G * splits;
-  p.block = kGemvRows;
-  p.lds_bytes = (32 * cpl * MP * 32 + 4) * 4;
-  p.ws_bytes = splits > 1 ? kWsCounterBytes * (((size_t)G * 4 + kWsCounterBytes - 1) / kWsCounterBytes) +
-                                (size_t)G * splits * M * kGemvRows * sizeof(int32_t)
-                          : 0;
+  p.block = 64 * kGemvWaves;
+  p.lds_bytes = lut_bytes > red_bytes ? lut_bytes : red_bytes;
+  p.ws_bytes = splits > 1 ? (size_t)M * N * sizeof(unsigned long long) : 0;
   return p;
 }
 
@@ -114,12 +134,7 @@ sherry_status run_gemm(const int8_t* x, const float* s_x, const void* packed, co
   args.M = (int)M;
   args.N = (int)N;
   args.K = (int)K;
-  if (plan.ws_bytes > 0) {
-    args.counters = static_cast<uint32_t*>(workspace);
-    const size_t cbytes =
-        kWsCounterBytes * (((size_t)plan.groups * 4 + kWsCounterBytes - 1) / kWsCounterBytes);
-    args.partials = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + cbytes);
-  }
+  if (plan.ws_bytes > 0) args.partials = static_cast<int32_t*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = plan.path == 0 ? launch_lut_gemv(plan, args, s) : launch_mfma_gemm(plan, args, s);
   return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
@@ -161,6 +176,14 @@ sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path, int* 
   if (block) *block = p.block;
   if (splits) *splits = p.splits;
   if (lds_bytes) *lds_bytes = p.lds_bytes;
+  return SHERRY_OK;
+}
+
+sherry_status sherry_gemm_plan_override(int rw, int ch, int splits) {
+  if (rw < 0 || ch < 0 || splits < 0 || (rw && rw != 1 && rw != 2 && rw != 4) ||
+      (ch && ch != 1 && ch != 2 && ch != 4 && ch != 8))
+    return SHERRY_ERR_SHAPE;
+  set_plan_override(rw, ch, splits);
   return SHERRY_OK;
 }
 

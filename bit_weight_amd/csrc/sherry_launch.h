@@ -9,20 +9,23 @@ namespace sherry {
 
 // Launch plan of the product for one shape (host-side, pure).
 struct GemmPlan {
-  int path;        // 0 = lookup-table GEMV, 1 = decode + int8 MFMA GEMM
-  int grid;        // workgroups
-  int block;       // threads per workgroup
-  int splits;      // K-splits per row group (GEMV)
-  int cpl;         // format k-tiles per lane per split (GEMV)
-  int groups;      // output row groups (GEMV)
-  int lds_bytes;   // dynamic + static LDS per workgroup
-  size_t ws_bytes; // workspace bytes required
+  int path;          // 0 = lookup-table GEMV, 1 = decode + int8 MFMA GEMM
+  int grid;          // workgroups
+  int block;         // threads per workgroup
+  int splits;        // K-splits per row group (GEMV)
+  int kt_per_split;  // format k-tiles per K-split (GEMV)
+  int rw;            // row tiles per workgroup (GEMV; 4 / rw waves share one)
+  int ch;            // k-tiles per LDS table stage (GEMV)
+  int groups;        // output row groups (GEMV)
+  int lds_bytes;     // dynamic LDS per workgroup
+  size_t ws_bytes;   // workspace bytes required
 };
 
 constexpr int kLutMaxM = 16;          // M <= 16 takes the lookup-table path
-constexpr int kGemvWaves = 4;         // waves (64 rows each) per GEMV workgroup
-constexpr int kGemvRows = 64 * kGemvWaves;
-constexpr size_t kWsCounterBytes = 256;  // alignment of the partials area
+constexpr int kGemvWaves = 4;         // waves per GEMV workgroup
+
+// Tuning override of the GEMV plan (0 = built-in choice), see sherry.h.
+void set_plan_override(int rw, int ch, int splits);
 
 GemmPlan plan_gemm(int M, int N, int K);
 
@@ -34,8 +37,7 @@ struct GemmArgs {
   float* y;            // fp32 output, or
   int32_t* acc;        // int32 output (exactly one of y / acc is non-null)
   int M, N, K;
-  uint32_t* counters;  // workspace: one arrival counter per row group
-  int32_t* partials;   // workspace: per-split int32 partial sums
+  int32_t* partials;   // workspace: zero-filled 64-bit accumulators [M,N] for K-splits
 };
 
 hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, float* alpha,

@@ -67,11 +67,11 @@ size_t sherry_packed_bytes(int64_t N, int64_t K);
 
 /* Bytes of scratch that sherry_gemm / sherry_gemm_i32 need for this shape
  * (0 when the chosen kernel needs none).  Host-only, pure.
- * The workspace must be zero-filled once before its first use; every
- * completed call leaves it ready for the next call (its counters return to
- * zero), so one zero-filled buffer of the largest size needed can serve any
- * sequence of calls on one stream.  Calls that run concurrently must not
- * share a workspace. */
+ * The workspace holds one 64-bit accumulator per output when the product is
+ * split along K.  It must be zero-filled once before its first use; every
+ * completed call leaves it zero-filled again, so one buffer of the largest
+ * size needed can serve any sequence of calls on one stream.  Calls that run
+ * concurrently must not share a workspace. */
 size_t sherry_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Offline compression (kernel 1), §3.1 and §2.1.
@@ -128,6 +128,18 @@ sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,
 sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path,
                                int* grid, int* block, int* splits,
                                int* lds_bytes);
+
+/* Tuning knob for benchmark sweeps (host-only).  Replaces the built-in
+ * launch plan of the lookup-table path for every later call in this process:
+ *   rw     row tiles per workgroup: 1, 2 or 4 (the workgroup's 4 waves are
+ *          rw row tiles x 4/rw waves sharing one); 0 = built-in choice.
+ *   ch     k-tiles (128 inputs) per LDS table stage: 1, 2, 4 or 8, capped
+ *          so one stage stays within 32 KB; 0 = built-in choice.
+ *   splits K-splits per output row group; 0 = built-in choice.
+ * Results do not depend on the plan.  sherry_workspace_bytes reflects the
+ * override, so query it after setting one.  Not thread-safe with respect to
+ * concurrent calls.  Returns SHERRY_ERR_SHAPE for an invalid value. */
+sherry_status sherry_gemm_plan_override(int rw, int ch, int splits);
 
 #ifdef __cplusplus
 }

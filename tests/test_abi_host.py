@@ -55,10 +55,26 @@ def test_plan_dispatch_rule():
         assert bw.plan(M, 4096, 4096)["path"] == "decode_mfma"
     p = bw.plan(1, 4096, 4096)
     assert p["block"] == 256 and p["grid"] >= 256
-    # the workspace covers the counters plus every split's partial sums
+    # the workspace holds one 64-bit accumulator per output when split
     if p["splits"] > 1:
-        assert bw.workspace_bytes(1, 4096, 4096) >= p["grid"] * 256 * 4
+        assert bw.workspace_bytes(1, 4096, 4096) == 4096 * 8
     assert bw.workspace_bytes(512, 14336, 4096) == 0
+
+
+def test_plan_override_changes_plan_and_workspace():
+    try:
+        base = bw.plan(1, 4096, 4096)
+        bw.plan_override(rw=2, ch=2, splits=8)
+        p = bw.plan(1, 4096, 4096)
+        assert p["splits"] == 8 and p["grid"] == 32 * 8
+        assert bw.workspace_bytes(1, 4096, 4096) == 4096 * 8
+        bw.plan_override(splits=1)
+        assert bw.workspace_bytes(1, 4096, 4096) == 0
+        with pytest.raises(bw.SherryError):
+            bw.plan_override(rw=3)
+    finally:
+        bw.plan_override()
+    assert bw.plan(1, 4096, 4096) == base
 
 
 def _gemm(**kw):

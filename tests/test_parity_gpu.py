@@ -125,6 +125,29 @@ def test_gemm_edges(orc, packed_cases, M, N, K):
     assert_y_close(gy.cpu().numpy(), y)
 
 
+PLANS = [(4, 1, 0), (4, 2, 3), (2, 2, 0), (2, 4, 2), (1, 1, 0), (1, 2, 5), (1, 8, 1), (4, 8, 1),
+         (2, 1, 7)]
+
+
+@pytest.mark.parametrize("rw,ch,splits", PLANS)
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 16])
+def test_gemm_lut_plans(orc, packed_cases, rw, ch, splits, M):
+    """Every LUT-GEMV launch shape (row tiles per workgroup, table stage size,
+    K-splits incl. ragged ones) gives the same exact result."""
+    N, K = 320, 1152                       # 5 row tiles, 9 k-tiles
+    T, alpha, packed, galpha = packed_cases[(N, K)]
+    q = synth.int8_uniform(M, K, seed=900 + M)
+    acc = orc.gemm_i32(q.numpy(), T)
+    try:
+        bw.plan_override(rw, ch, splits)
+        _say(f"plan override rw={rw} ch={ch} splits={splits} M={M}: {bw.plan(M, N, K)}")
+        gacc = bw.gemm_i32(q.cuda(), packed, N, K)
+        torch.cuda.synchronize()
+    finally:
+        bw.plan_override()
+    assert np.array_equal(gacc.cpu().numpy(), acc)
+
+
 def test_gemm_extreme_activations(orc, packed_cases):
     N, K = 192, 384
     T, alpha, packed, galpha = packed_cases[(N, K)]
