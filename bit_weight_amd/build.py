@@ -5,7 +5,8 @@
 Every HIP source under csrc/ is compiled for gfx950 only and linked into
 bit_weight_amd/libsherry.so.  Packed-FP32 instruction selection is switched
 off for device code (-packed-fp32-ops); hipcc's host pass warns that it does
-not know that feature, which is harmless.
+not know that feature, which is harmless.  MFMA accumulators are kept in arch
+VGPRs (-amdgpu-mfma-vgpr-form).
 """
 
 from __future__ import annotations
@@ -22,6 +23,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in arch VGPRs: the matrix ops then accumulate in
+    # place instead of shuffling accumulation registers every k-step
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -57,13 +57,12 @@ void set_plan_override(int rw, int ch, int splits) {
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   if (M > kLutMaxM) {
-    constexpr int BM = 128, BN = 128;
     p.path = 1;
-    p.grid = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+    p.grid = mfma_gemm_grid(M, N);
     p.block = 256;
     p.splits = 1;
     p.kt_per_split = K / kTileK;
-    p.lds_bytes = (BM + BN) * (kTileK + 16) + 32 * 4;
+    p.lds_bytes = 16 * (448 + 4) * 4;  // epilogue tile, the largest LDS use
     p.ws_bytes = 0;
     return p;
   }

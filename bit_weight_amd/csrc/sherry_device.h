@@ -43,6 +43,15 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[5], int j) {
   return __builtin_amdgcn_alignbit(w[d + 1], w[d], sh) & 31u;
 }
 
+// Workgroup barrier that orders only LDS accesses.  __syncthreads() also
+// orders global memory, so it waits for every global load in flight; this
+// one leaves prefetched loads outstanding across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Byte offset of format tile (rt, kt) for a matrix with K columns.
 __device__ __forceinline__ size_t tile_offset(int rt, int kt, int KT) {
   return ((size_t)rt * (size_t)KT + (size_t)kt) * (size_t)kTileBytes;

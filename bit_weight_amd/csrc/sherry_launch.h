@@ -45,6 +45,7 @@ hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, f
 hipError_t launch_quantize_act(const float* x, int M, int K, int8_t* q, float* s_x,
                                hipStream_t stream);
 hipError_t launch_lut_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
+int mfma_gemm_grid(int M, int N);
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 
 }  // namespace sherry
