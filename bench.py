@@ -54,8 +54,13 @@ def parse():
 
 
 def copies_for(packed_bytes: int, requested: int) -> int:
+    """Rotating weight copies: enough to exceed twice the last-level cache, so
+    each launch streams its weights from HBM.  Weights under 1 MiB (the
+    latency-bound smallest workload) are not rotated."""
     if requested > 0:
         return requested
+    if packed_bytes < (1 << 20):
+        return 2
     return max(2, math.ceil(2 * MALL_BYTES / packed_bytes) + 1)
 
 
@@ -125,19 +130,30 @@ def algorithmic_bytes(w) -> int:
     return w.packed_bytes + 4 * w.N + w.M * w.K + 4 * w.M + 4 * w.M * w.N
 
 
-def kernel_sources_sha() -> str:
+KERNEL_SOURCES = {
+    "lut_gemv": ("lut_gemv.hip", "sherry_device.h", "sherry_launch.h"),
+    "mfma_gemm": ("mfma_gemm.hip", "sherry_device.h", "sherry_launch.h"),
+}
+
+
+def kernel_sources_sha(kernel: str) -> str:
+    """Hash of the sources one product kernel is built from."""
     h = hashlib.sha256()
-    for f in ("lut_gemv.hip", "mfma_gemm.hip", "sherry_device.h", "sherry_abi.hip"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "bit_weight_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_tag: str):
+def plan_tag(plan: dict) -> str:
+    return f"grid={plan['grid']} block={plan['block']} splits={plan['splits']} lds={plan['lds_bytes']}"
+
+
+def traffic_from_profile(kernel: str, workload: str, plan: dict):
     """HBM bytes per launch measured with rocprofv3 counters, read from the
-    committed summary under profiles/; None if absent or if the kernel
-    sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+    committed summary under profiles/; None if absent, or if the kernel's
+    sources or its launch plan changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -146,7 +162,9 @@ def traffic_from_profile(kernel_tag: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_sources_sha") != kernel_sources_sha():
+    if vals.get("kernel_sources_sha") != kernel_sources_sha(kernel):
+        return None
+    if vals.get("plan") != plan_tag(plan):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -250,7 +268,7 @@ def main():
     act_ms, _ = graph_time(torch, lambda i: bw.quantize_act(st.x), n_k, reps=3)
     alg = algorithmic_bytes(w)
     achieved = alg / gemm_ms / 1e6
-    traffic = traffic_from_profile(f"lut_gemv_{name}")
+    traffic = traffic_from_profile("lut_gemv", name, bw.plan(w.M, w.N, w.K))
     value = w.packed_bytes / step_ms / 1e6
     out = {
         "metric": METRIC,
@@ -308,7 +326,9 @@ def main():
                           "value": p5["TOPS"], "unit": "TOPS",
                           "roofline": {"bound": "mfma", "achieved": p5["TOPS"],
                                        "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                                       "frac": p5["mfma_frac"], "traffic": None,
+                                       "frac": p5["mfma_frac"],
+                                       "traffic": traffic_from_profile(
+                                           "mfma_gemm", "5", p5["plan"]),
                                        "kernel": "mfma_gemm_kernel"}}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)

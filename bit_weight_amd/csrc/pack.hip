@@ -81,37 +81,67 @@ __global__ __launch_bounds__(256) void pack_alpha_kernel(const float* __restrict
 }
 
 // One workgroup per token: s = max|x| / 127, q = clamp(rint(x / s), +-127).
+// Every thread issues all of its loads before the first use, so a token costs
+// one memory round trip; the values stay in registers for the second pass.
+// J = float4 slots per thread (J * 1024 >= K); J = 0 is the looping form for
+// rows longer than the register path holds.
+__device__ __forceinline__ char4 quant4(const float4 v, float s) {
+  char4 o;
+  o.x = (signed char)fminf(fmaxf(rintf(v.x / s), -127.0f), 127.0f);
+  o.y = (signed char)fminf(fmaxf(rintf(v.y / s), -127.0f), 127.0f);
+  o.z = (signed char)fminf(fmaxf(rintf(v.z / s), -127.0f), 127.0f);
+  o.w = (signed char)fminf(fmaxf(rintf(v.w / s), -127.0f), 127.0f);
+  return o;
+}
+
+__device__ __forceinline__ float amax4(const float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__device__ __forceinline__ float block_amax(float amax, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+template <int J>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x,
                                                            int8_t* __restrict__ q,
                                                            float* __restrict__ s_x, int K) {
   __shared__ float red[4];
   const int m = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)m * K);
+  char4* qr = reinterpret_cast<char4*>(q + (size_t)m * K);
   const int K4 = K / 4;
   float amax = 0.0f;
-  for (int i = threadIdx.x; i < K4; i += blockDim.x) {
-    const float4 v = xr[i];
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
+  if constexpr (J > 0) {
+    float4 v[J];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const bool zero = !(amax > 0.0f);
-  const float s = zero ? 1.0f : amax / 127.0f;
-  if (threadIdx.x == 0) s_x[m] = s;
-  char4* qr = reinterpret_cast<char4*>(q + (size_t)m * K);
-  for (int i = threadIdx.x; i < K4; i += blockDim.x) {
-    const float4 v = xr[i];
-    char4 o = make_char4(0, 0, 0, 0);
-    if (!zero) {
-      o.x = (signed char)fminf(fmaxf(rintf(v.x / s), -127.0f), 127.0f);
-      o.y = (signed char)fminf(fmaxf(rintf(v.y / s), -127.0f), 127.0f);
-      o.z = (signed char)fminf(fmaxf(rintf(v.z / s), -127.0f), 127.0f);
-      o.w = (signed char)fminf(fmaxf(rintf(v.w / s), -127.0f), 127.0f);
+    for (int j = 0; j < J; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      v[j] = i < K4 ? xr[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    qr[i] = o;
+#pragma unroll
+    for (int j = 0; j < J; ++j) amax = fmaxf(amax, amax4(v[j]));
+    amax = block_amax(amax, red);
+    const bool zero = !(amax > 0.0f);
+    const float s = zero ? 1.0f : amax / 127.0f;
+    if (threadIdx.x == 0) s_x[m] = s;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      if (i < K4) qr[i] = zero ? make_char4(0, 0, 0, 0) : quant4(v[j], s);
+    }
+  } else {
+    for (int i = threadIdx.x; i < K4; i += 256) amax = fmaxf(amax, amax4(xr[i]));
+    amax = block_amax(amax, red);
+    const bool zero = !(amax > 0.0f);
+    const float s = zero ? 1.0f : amax / 127.0f;
+    if (threadIdx.x == 0) s_x[m] = s;
+    for (int i = threadIdx.x; i < K4; i += 256)
+      qr[i] = zero ? make_char4(0, 0, 0, 0) : quant4(xr[i], s);
   }
 }
 
@@ -130,7 +160,15 @@ hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, f
 
 hipError_t launch_quantize_act(const float* x, int M, int K, int8_t* q, float* s_x,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(quantize_act_kernel, dim3(M), dim3(256), 0, stream, x, q, s_x, K);
+  const int slots = (K / 4 + 255) / 256;
+  const dim3 grid(M), block(256);
+  if (slots <= 1) hipLaunchKernelGGL(quantize_act_kernel<1>, grid, block, 0, stream, x, q, s_x, K);
+  else if (slots <= 2) hipLaunchKernelGGL(quantize_act_kernel<2>, grid, block, 0, stream, x, q, s_x, K);
+  else if (slots <= 4) hipLaunchKernelGGL(quantize_act_kernel<4>, grid, block, 0, stream, x, q, s_x, K);
+  else if (slots <= 8) hipLaunchKernelGGL(quantize_act_kernel<8>, grid, block, 0, stream, x, q, s_x, K);
+  else if (slots <= 12) hipLaunchKernelGGL(quantize_act_kernel<12>, grid, block, 0, stream, x, q, s_x, K);
+  else if (slots <= 16) hipLaunchKernelGGL(quantize_act_kernel<16>, grid, block, 0, stream, x, q, s_x, K);
+  else hipLaunchKernelGGL(quantize_act_kernel<0>, grid, block, 0, stream, x, q, s_x, K);
   return hipGetLastError();
 }
 
