@@ -14,10 +14,12 @@ HIP events (recorded on the stream the kernels run on) around the replay.
 Prints ONE JSON line.  `value` is packed-weight GB/s of the whole step
 (N*K*5/32 bytes per step / step time) on the default workload (decode GEMV,
 LLaMA-7B attention projection: M=1, K=4096, N=4096).  "roofline" is the
-dominant kernel (the LUT-GEMV) against the 8 TB/s HBM peak; "prefill" holds
-the M=512 decode + int8 MFMA product against the 5.0 POP/s int8 peak;
-"workloads" holds every workload's kernel time.  "cpu_baseline" times the CPU
-oracle (single thread) on a bounded sample of the same workload.
+dominant kernel (the product kernel the launch plan picks for that shape)
+against the 8 TB/s HBM peak; "prefill" holds the M=512 decode + int8 MFMA
+product against the 5.0 POP/s int8 peak; "workloads" holds every workload's
+kernel time, and for M <= 16 the time of each small-M path (lookup-table
+GEMV and matrix-core GEMV).  "cpu_baseline" times the CPU oracle (single
+thread) on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -132,8 +134,11 @@ def algorithmic_bytes(w) -> int:
 
 KERNEL_SOURCES = {
     "lut_gemv": ("lut_gemv.hip", "sherry_device.h", "sherry_launch.h"),
+    "mfma_gemv": ("mfma_gemv.hip", "sherry_device.h", "sherry_launch.h"),
     "mfma_gemm": ("mfma_gemm.hip", "sherry_device.h", "sherry_launch.h"),
 }
+# plan path -> kernel tag
+PATH_KERNEL = {"lut_gemv": "lut_gemv", "decode_mfma_gemv": "mfma_gemv", "decode_mfma": "mfma_gemm"}
 
 
 def kernel_sources_sha(kernel: str) -> str:
@@ -268,7 +273,9 @@ def main():
     act_ms, _ = graph_time(torch, lambda i: bw.quantize_act(st.x), n_k, reps=3)
     alg = algorithmic_bytes(w)
     achieved = alg / gemm_ms / 1e6
-    traffic = traffic_from_profile("lut_gemv", name, bw.plan(w.M, w.N, w.K))
+    plan = bw.plan(w.M, w.N, w.K)
+    kern = PATH_KERNEL[plan["path"]]
+    traffic = traffic_from_profile(kern, name, plan)
     value = w.packed_bytes / step_ms / 1e6
     out = {
         "metric": METRIC,
@@ -291,7 +298,7 @@ def main():
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "lut_gemv_kernel",
+                     "traffic": traffic, "kernel": f"{kern}_kernel",
                      "kernel_us": round(gemm_ms * 1e3, 3), "bytes_per_launch": alg,
                      "packed_bytes_per_launch": w.packed_bytes},
         "kernels_us": {"sherry_gemm": round(gemm_ms * 1e3, 3),
@@ -311,6 +318,19 @@ def main():
             ww = s2.w
             ent = {"M": ww.M, "K": ww.K, "N": ww.N, "kernel_us": round(ms * 1e3, 3),
                    "plan": bw.plan(ww.M, ww.N, ww.K), "rotating_copies": s2.R}
+            if ww.M <= 16:
+                # every small-M path on the same launches (the default is one of them)
+                alt = {}
+                for path in ("lut_gemv", "decode_mfma_gemv"):
+                    try:
+                        bw.plan_override(path)
+                        s2.ws = torch.zeros(max(bw.workspace_bytes(ww.M, ww.N, ww.K), 256),
+                                            dtype=torch.uint8, device="cuda")
+                        ms_p, _ = graph_time(torch, lambda i: s2.gemm(bw, i), max(200, s2.R), reps=3)
+                        alt[path] = round(ms_p * 1e3, 3)
+                    finally:
+                        bw.plan_override()
+                ent["path_us"] = alt
             if ww.M > 16:
                 tops = 2.0 * ww.M * ww.N * ww.K / ms / 1e9
                 ent.update({"TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})

@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
                 "sherry_packed_bytes": ([i64, i64], sz),
                 "sherry_workspace_bytes": ([i64, i64, i64], sz),
                 "sherry_gemm_plan": ([i64, i64, i64, ip, ip, ip, ip, ip], ci),
-                "sherry_gemm_plan_override": ([ci, ci, ci], ci),
+                "sherry_gemm_plan_override": ([ci, ci, ci, ci], ci),
                 "sherry_quantize_pack": ([vp, i64, i64, vp, vp, vp], ci),
                 "sherry_quantize_act": ([vp, i64, i64, vp, vp, vp], ci),
                 "sherry_gemm": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
@@ -117,13 +117,19 @@ def plan(M: int, N: int, K: int) -> dict:
     vals = [ctypes.c_int() for _ in range(5)]
     _check(lib().sherry_gemm_plan(M, N, K, *[ctypes.byref(v) for v in vals]), "sherry_gemm_plan")
     path, grid, block, splits, lds = (v.value for v in vals)
-    return {"path": "lut_gemv" if path == 0 else "decode_mfma", "grid": grid,
+    return {"path": PATHS.get(path, str(path)), "grid": grid,
             "block": block, "splits": splits, "lds_bytes": lds}
 
 
-def plan_override(rw: int = 0, ch: int = 0, splits: int = 0) -> None:
-    """Tuning knob: force the LUT-GEMV launch plan (0 = built-in choice)."""
-    _check(lib().sherry_gemm_plan_override(rw, ch, splits), "sherry_gemm_plan_override")
+PATHS = {0: "lut_gemv", 1: "decode_mfma", 2: "decode_mfma_gemv"}
+PATH_IDS = {v: k for k, v in PATHS.items()}
+
+
+def plan_override(path=None, rw: int = 0, ch: int = 0, splits: int = 0) -> None:
+    """Tuning knob for M <= 16: force a path ("lut_gemv", "decode_mfma",
+    "decode_mfma_gemv" or None = built-in) and its launch plan (0 = built-in)."""
+    pid = -1 if path is None else PATH_IDS[path]
+    _check(lib().sherry_gemm_plan_override(pid, rw, ch, splits), "sherry_gemm_plan_override")
 
 
 def quantize_pack(W: torch.Tensor):

@@ -176,25 +176,46 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
   if (!active) return;
   const int n = rt * kTileRows + lane;
   const float al = a.y ? a.alpha[n] : 0.0f;
+  // every token's atomic is issued before any result is used: one memory
+  // round trip per lane whatever M is
+  int total[2 * MP];
+  bool last[2 * MP];
 #pragma unroll
   for (int m = 0; m < 2 * MP; ++m) {
-    if (m >= M) continue;
-    int total = acc[m];
-    if (splits > 1) {
-      unsigned long long* cell = reinterpret_cast<unsigned long long*>(a.partials) + (size_t)m * N + n;
-      const unsigned long long inc = (1ull << 32) + (unsigned long long)(long long)acc[m];
-      const unsigned long long now =
-          __hip_atomic_fetch_add(cell, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
-      total = (int)(uint32_t)now;
-      const long long count = ((long long)now - (long long)total) >> 32;
-      if (count != splits) continue;
-      __hip_atomic_store(cell, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    total[m] = acc[m];
+    last[m] = true;
+  }
+  if (splits > 1) {
+    unsigned long long now[2 * MP];
+#pragma unroll
+    for (int m = 0; m < 2 * MP; ++m) {
+      now[m] = 0;
+      if (m < M) {
+        unsigned long long* cell = reinterpret_cast<unsigned long long*>(a.partials) + (size_t)m * N + n;
+        const unsigned long long inc = (1ull << 32) + (unsigned long long)(long long)acc[m];
+        now[m] = __hip_atomic_fetch_add(cell, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
+    // (no result is touched before the last atomic is issued)
+#pragma unroll
+    for (int m = 0; m < 2 * MP; ++m) {
+      now[m] += (1ull << 32) + (unsigned long long)(long long)acc[m];
+      total[m] = (int)(uint32_t)now[m];
+      const long long count = ((long long)now[m] - (long long)total[m]) >> 32;
+      last[m] = count == splits;
+      if (m < M && last[m])
+        __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.partials) + (size_t)m * N + n, 0ull,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2 * MP; ++m) {
+    if (m >= M || !last[m]) continue;
     if (a.y) {
-      const float t = (float)total * a.s_x[m];
+      const float t = (float)total[m] * a.s_x[m];
       a.y[(size_t)m * N + n] = t * al;
     } else {
-      a.acc[(size_t)m * N + n] = total;
+      a.acc[(size_t)m * N + n] = total[m];
     }
   }
 }

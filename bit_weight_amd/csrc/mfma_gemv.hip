@@ -1,0 +1,255 @@
+// Small-M (decode, M <= 16) product on the matrix cores: the 5-bit codes
+// are decoded to int8 {-1,0,+1} in registers and contracted with the int8
+// activations by v_mfma_i32_16x16x64_i8, the M tokens padded to the
+// instruction's 16 rows.  y = ((float)acc * s_x[m]) * alpha[n] as in every
+// path.  [Sherry page §2.2] computes the same integer sums through
+// per-segment tables of pattern dot products; on gfx950 a decoded code pair
+// feeds 8 multiply-adds per token of a matrix-core instruction for one LDS
+// lookup and two VALU ops, where a table lookup costs one LDS read and about
+// three VALU ops per block and token pair, so this form streams the codes at
+// a higher rate.
+//
+// Mapping (wave64):
+//  * A workgroup owns one format row tile (64 weight rows = 4 MFMA column
+//    blocks of 16) and one K-split; its KW waves (4, 8 or 16) take the
+//    split's k-tiles (128 inputs each) in turn, so many waves stream one row
+//    tile and the whole grid keeps enough bytes in flight to cover HBM
+//    latency.  The waves add their sums through LDS at the end; K-splits
+//    across workgroups add theirs with the one-round-trip 64-bit atomic
+//    count used by the lookup-table GEMV.
+//  * B operand: lane l of a column block holds weight row l % 16; lane group
+//    g = l / 16 takes codes 8g..8g+7 of the k-tile (the first four in MFMA
+//    sub-step 0, the rest in sub-step 1).  Those 40 bits lie in dwords g and
+//    g+1 of the row's 160-bit string.  A wave loads its tile coalesced, lane
+//    r = tile row r (16 + 4 bytes), and moves dwords g and g+1 of rows
+//    16t..16t+15 to lane group g of block t with two 4 x 4 transposes of
+//    16-lane rows (v_permlane32_swap, then v_permlane16_swap).  A 1024-entry
+//    LDS table maps a 10-bit code pair to its 8 int8 weights.
+//  * A operand: lane (l % 16, g) holds token l % 16, inputs 32g + 16s .. +15
+//    of the k-tile in sub-step s (the same input order as B, which the dot
+//    product does not see).  Loaded straight from global memory through a
+//    buffer descriptor whose range ends at token M, so the padding tokens
+//    read as zero without a branch.
+//  * Codes and activations are prefetched four k-tiles ahead into four
+//    register stages used in turn, so each wave keeps ~5 KB of its codes in
+//    flight (HBM streaming needs bytes in flight x latency to cover the
+//    bandwidth).
+#include "sherry_device.h"
+#include "sherry_launch.h"
+
+namespace sherry {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kBlk = kTileRows / 16;   // MFMA column blocks per wave
+constexpr int kStages = 4;             // k-tiles of codes and activations in flight per wave
+constexpr int kRedLd = kTileRows + 4;  // words per token row of the epilogue tile
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, size_t bytes) {
+  const int n = bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// B operand of one sub-step: 4 codes (20 bits of v) as two code pairs.
+__device__ __forceinline__ v4i decode4(uint32_t v, const uint8_t* dec2) {
+  const uint2 e0 = *reinterpret_cast<const uint2*>(dec2 + ((v << 3) & 0x1FF8u));
+  const uint2 e1 = *reinterpret_cast<const uint2*>(dec2 + ((v >> 7) & 0x1FF8u));
+  return v4i{(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
+}
+
+// 4 x 4 transpose of 16-lane rows: out[t] row g = in[g] row t.
+__device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                           uint32_t (&out)[4]) {
+  // swap the upper 32 lanes of the first operand with the lower 32 of the second
+  const auto s02 = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+  // swap the odd 16-lane rows of the first operand with the even rows of the second
+  const auto t01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  const auto t23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  out[0] = t01[0];
+  out[1] = t01[1];
+  out[2] = t23[0];
+  out[3] = t23[1];
+}
+
+// KW waves share one row tile; MT = the token count rounded up to a power
+// of two (1..16).
+template <int KW, int MT>
+__global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int splits, int kt_per_split) {
+  __shared__ __attribute__((aligned(16))) uint2 dec2[1024];
+  __shared__ __attribute__((aligned(16))) int red[KW * MT * kRedLd];   // [wave][token][row]
+
+  const int M = a.M, N = a.N, K = a.K, KT = K / kTileK;
+  const int rt = blockIdx.x / splits;
+  const int s = blockIdx.x - rt * splits;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int q = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar offsets
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const int kt_begin = s * kt_per_split;
+  const int kt_end = min(KT, kt_begin + kt_per_split);
+  const int span = kt_end - kt_begin;
+  const int nk = span > q ? (span - q + KW - 1) / KW : 0;
+
+  // buffer descriptors: this row tile's codes, and the M tokens of x
+  const size_t tb = tile_offset(rt, 0, KT);
+  const __amdgpu_buffer_rsrc_t rc = gemv_rsrc(a.packed + tb, (size_t)KT * kTileBytes);
+  const __amdgpu_buffer_rsrc_t rx = gemv_rsrc(a.x, (size_t)M * (size_t)K);
+  // lane offset of the activations (>= M*K for the padding tokens; the
+  // k-tile offset is added to it, not passed as the scalar offset, so the
+  // descriptor's range check sees the whole offset)
+  const int x_v = l16 * K + 32 * g;
+  const uint32_t sh = 8u * (uint32_t)g;      // bit 40g mod 32
+
+  // i-th k-tile of this wave (clamped: the prefetch past the end re-reads
+  // the last tile, whose values are never used)
+  auto load = [&](int i, v4u& w, uint32_t& h, v4u& x0, v4u& x1) {
+    const int kt = kt_begin + q + KW * min(i, nk - 1);
+    const int ks = kt * kTileBytes, ka = kt * kTileK;
+    w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
+    h = __builtin_amdgcn_raw_buffer_load_b32(rc, kTileHiOff + 4 * lane, ks, 0);
+    x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka, 0, 0);
+    x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka + 16, 0, 0);
+  };
+
+  v4i acc[kBlk];
+#pragma unroll
+  for (int t = 0; t < kBlk; ++t) acc[t] = v4i{0, 0, 0, 0};
+
+  // kStages register stages, filled kStages k-tiles ahead and used in turn.
+  // The scheduling barriers keep every refill inside its own step, so a step
+  // waits only for its own stage while the newer ones stay in flight.
+  v4u cw[kStages];
+  uint32_t ch[kStages];
+  v4u xa[kStages], xb[kStages];
+  if (nk > 0) {
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) {
+      load(st, cw[st], ch[st], xa[st], xb[st]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  for (int i = tid; i < 1024; i += 64 * KW) dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
+  lds_barrier();
+  const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
+
+  auto step = [&](int i, v4u& w, uint32_t& h, v4u& x0, v4u& x1) {
+    // lane (l16, g) of block t <- dwords g (lo) and g+1 (hi) of row 16t+l16
+    uint32_t lo[kBlk], hi[kBlk];
+    transpose4(w.x, w.y, w.z, w.w, lo);
+    transpose4(w.y, w.z, w.w, h, hi);
+    uint32_t f0[kBlk], f1[kBlk];
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t) {
+      const uint32_t v = __builtin_amdgcn_alignbit(hi[t], lo[t], sh);
+      f0[t] = v;
+      f1[t] = __builtin_amdgcn_alignbit(hi[t] >> sh, v, 20);
+    }
+    const v4i a0 = __builtin_bit_cast(v4i, x0), a1 = __builtin_bit_cast(v4i, x1);
+    load(i + kStages, w, h, x0, x1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t)
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, decode4(f0[t], d2), acc[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t)
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, decode4(f1[t], d2), acc[t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int i = 0;
+  for (; i + kStages <= nk; i += kStages) {
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) step(i + st, cw[st], ch[st], xa[st], xb[st]);
+  }
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (i + st < nk) step(i + st, cw[st], ch[st], xa[st], xb[st]);
+
+  // Epilogue.  Every wave writes its sums to LDS as [token][row]; then each
+  // lane owns one weight row and a fixed set of tokens, so the K-split
+  // atomics of a lane are issued back to back with no branch between them
+  // and cost one memory round trip.  Tokens from M up to the padded count MT
+  // add 0 to the cell of token M-1, which changes nothing.
+#pragma unroll
+  for (int t = 0; t < kBlk; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * g + j < MT) red[(q * MT + 4 * g + j) * kRedLd + 16 * t + l16] = acc[t][j];
+  __syncthreads();
+  constexpr int TPW = MT >= KW ? MT / KW : 1;        // tokens per wave
+  if (q * TPW >= MT) return;
+  const int n = rt * kTileRows + lane;
+  const float al = a.y ? a.alpha[n] : 0.0f;
+  int total[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int m = q * TPW + i;
+    int v = 0;
+#pragma unroll
+    for (int qq = 0; qq < KW; ++qq) v += red[(qq * MT + m) * kRedLd + lane];
+    total[i] = v;
+  }
+  bool last[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) last[i] = true;
+  if (splits > 1) {
+    unsigned long long* cells = reinterpret_cast<unsigned long long*>(a.partials);
+    unsigned long long now[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int m = q * TPW + i;
+      const unsigned long long inc =
+          m < M ? (1ull << 32) + (unsigned long long)(long long)total[i] : 0ull;
+      now[i] = __hip_atomic_fetch_add(cells + (size_t)min(m, M - 1) * N + n, inc, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int m = q * TPW + i;
+      now[i] += (1ull << 32) + (unsigned long long)(long long)total[i];
+      total[i] = (int)(uint32_t)now[i];
+      // the high word minus the borrow of a negative low word = arrivals
+      last[i] = (((long long)now[i] - (long long)total[i]) >> 32) == (long long)splits;
+      if (m < M && last[i])
+        __hip_atomic_store(cells + (size_t)m * N + n, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int m = q * TPW + i;
+    if (m >= M || !last[i]) continue;
+    if (a.y) {
+      const float tv = (float)total[i] * a.s_x[m];
+      a.y[(size_t)m * N + n] = tv * al;
+    } else {
+      a.acc[(size_t)m * N + n] = total[i];
+    }
+  }
+}
+
+template <int KW>
+hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  const dim3 grid(p.grid), block(64 * KW);
+  if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// plan.rw carries the waves per row tile for this path (4, 8 or 16).
+hipError_t launch_mfma_gemv(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  switch (p.rw) {
+    case 4: return launch_kw<4>(p, a, stream);
+    case 8: return launch_kw<8>(p, a, stream);
+    case 16: return launch_kw<16>(p, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sherry

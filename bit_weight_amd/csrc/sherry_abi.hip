@@ -45,10 +45,50 @@ bool shape_ok(int64_t M, int64_t N, int64_t K) {
 }  // namespace
 
 namespace {
-std::atomic<int> g_ovr_rw{0}, g_ovr_ch{0}, g_ovr_splits{0};
-}
+std::atomic<int> g_ovr_path{-1}, g_ovr_rw{0}, g_ovr_ch{0}, g_ovr_splits{0};
 
-void set_plan_override(int rw, int ch, int splits) {
+// Small-M path: decode + int8 MFMA GEMV.  One row tile per workgroup and
+// KW waves taking turns over its k-tiles.  With >= 128 row tiles, 8 waves
+// per row tile and no K-split already keep >= 1024 waves streaming; smaller
+// N uses 4 waves per row tile and splits K until there are >= 1024 waves and
+// each wave has at most ~3 k-tiles (measured on MI355X at the LLaMA shapes).
+GemmPlan plan_mfma_gemv(int M, int N, int K) {
+  GemmPlan p{};
+  const int KT = K / kTileK, RT = N / kTileRows;
+  const int ovr_kw = g_ovr_rw.load();
+  const int kw = ovr_kw == 4 || ovr_kw == 8 || ovr_kw == 16 ? ovr_kw : (RT >= 128 ? 8 : 4);
+  int splits = 1;
+  if (g_ovr_splits.load() > 0) {
+    splits = g_ovr_splits.load();
+  } else if (RT < 128) {
+    const int by_waves = (1024 + RT * kw - 1) / (RT * kw);
+    const int by_depth = (KT + 3 * kw - 1) / (3 * kw);
+    splits = by_waves > by_depth ? by_waves : by_depth;
+    const int max_splits = KT / kw > 0 ? KT / kw : 1;   // >= one k-tile per wave
+    if (splits > max_splits) splits = max_splits;
+  }
+  if (splits > KT) splits = KT;
+  if (splits < 1) splits = 1;
+  const int kt_per_split = (KT + splits - 1) / splits;
+  splits = (KT + kt_per_split - 1) / kt_per_split;
+  int mt = 1;
+  while (mt < M) mt *= 2;
+  p.path = 2;
+  p.groups = RT;
+  p.rw = kw;            // waves per row tile on this path
+  p.ch = 1;
+  p.splits = splits;
+  p.kt_per_split = kt_per_split;
+  p.grid = RT * splits;
+  p.block = 64 * kw;
+  p.lds_bytes = 1024 * 8 + kw * mt * (kTileRows + 4) * 4;   // static: pair table + reduction
+  p.ws_bytes = splits > 1 ? (size_t)M * N * sizeof(unsigned long long) : 0;
+  return p;
+}
+}  // namespace
+
+void set_plan_override(int path, int rw, int ch, int splits) {
+  g_ovr_path = path;
   g_ovr_rw = rw;
   g_ovr_ch = ch;
   g_ovr_splits = splits;
@@ -66,6 +106,12 @@ GemmPlan plan_gemm(int M, int N, int K) {
     p.ws_bytes = 0;
     return p;
   }
+  const int path = g_ovr_path.load() >= 0 ? g_ovr_path.load() : kDefaultSmallMPath;
+  if (path == 1) {
+    GemmPlan q = plan_gemm(kLutMaxM + 1, N, K);
+    return q;
+  }
+  if (path == 2) return plan_mfma_gemv(M, N, K);
   const int MP = (M + 1) / 2;
   const int KT = K / kTileK;
   const int RT = N / kTileRows;
@@ -135,7 +181,9 @@ sherry_status run_gemm(const int8_t* x, const float* s_x, const void* packed, co
   args.K = (int)K;
   if (plan.ws_bytes > 0) args.partials = static_cast<int32_t*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = plan.path == 0 ? launch_lut_gemv(plan, args, s) : launch_mfma_gemm(plan, args, s);
+  const hipError_t e = plan.path == 0   ? launch_lut_gemv(plan, args, s)
+                       : plan.path == 2 ? launch_mfma_gemv(plan, args, s)
+                                        : launch_mfma_gemm(plan, args, s);
   return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
 }
 
@@ -178,11 +226,12 @@ sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path, int* 
   return SHERRY_OK;
 }
 
-sherry_status sherry_gemm_plan_override(int rw, int ch, int splits) {
-  if (rw < 0 || ch < 0 || splits < 0 || (rw && rw != 1 && rw != 2 && rw != 4) ||
+sherry_status sherry_gemm_plan_override(int path, int rw, int ch, int splits) {
+  if (path < -1 || path > 2 || rw < 0 || ch < 0 || splits < 0 ||
+      (rw && rw != 1 && rw != 2 && rw != 4 && rw != 8 && rw != 16) ||
       (ch && ch != 1 && ch != 2 && ch != 4 && ch != 8))
     return SHERRY_ERR_SHAPE;
-  set_plan_override(rw, ch, splits);
+  set_plan_override(path, rw, ch, splits);
   return SHERRY_OK;
 }
 

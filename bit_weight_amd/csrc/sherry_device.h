@@ -28,12 +28,27 @@ __host__ __device__ constexpr int code_value(int c, int j) {
   return (c & 1) ? -v : v;
 }
 
-// The block of code c as 4 int8 lanes of a dword (byte j = position j).
-__host__ __device__ constexpr uint32_t code_word(int c) {
-  uint32_t w = 0;
-  for (int j = 0; j < 4; ++j) w |= (uint32_t)(uint8_t)(int8_t)code_value(c, j) << (8 * j);
-  return w;
+// The block of code c as 4 int8 lanes of a dword (byte j = position j),
+// without branches: the three nonzeros' bytes (0x01 or 0xFF) in order, then
+// a zero byte inserted at position z.
+__host__ __device__ constexpr uint32_t code_word(uint32_t c) {
+  const uint32_t s = c & 1u, r2 = (c >> 1) & 1u, r1 = (c >> 2) & 1u, z = (c >> 3) & 3u;
+  const uint32_t n1 = s, n2 = s ^ r1, n3 = s ^ r2;          // 1 = negative
+  const uint32_t v3 = (0x010101u | (n1 * 0xFEu) | (n2 * 0xFE00u) | (n3 * 0xFE0000u));
+  const uint32_t below = (1u << (8u * z)) - 1u;             // bytes before z
+  return (v3 & below) | ((v3 << 8) & ~(below | (0xFFu << (8u * z))));
 }
+
+// The closed form above agrees with the definition for all 32 codes.
+__host__ __device__ constexpr bool code_word_matches_definition() {
+  for (int c = 0; c < 32; ++c) {
+    uint32_t w = 0;
+    for (int j = 0; j < 4; ++j) w |= (uint32_t)(uint8_t)(int8_t)code_value(c, j) << (8 * j);
+    if (w != code_word((uint32_t)c)) return false;
+  }
+  return true;
+}
+static_assert(code_word_matches_definition(), "code_word disagrees with code_value");
 
 // 5-bit code j (0..31) of a row's 160-bit string held in w[0..4].  Called
 // with a compile-time j inside unrolled loops, so the branch folds away.

@@ -9,23 +9,26 @@ namespace sherry {
 
 // Launch plan of the product for one shape (host-side, pure).
 struct GemmPlan {
-  int path;          // 0 = lookup-table GEMV, 1 = decode + int8 MFMA GEMM
+  int path;          // 0 = lookup-table GEMV, 1 = decode + int8 MFMA GEMM,
+                     // 2 = decode + int8 MFMA GEMV (M <= 16)
   int grid;          // workgroups
   int block;         // threads per workgroup
   int splits;        // K-splits per row group (GEMV)
   int kt_per_split;  // format k-tiles per K-split (GEMV)
-  int rw;            // row tiles per workgroup (GEMV; 4 / rw waves share one)
+  int rw;            // row tiles per workgroup (GEMVs; 4 / rw waves share one)
   int ch;            // k-tiles per LDS table stage (GEMV)
   int groups;        // output row groups (GEMV)
   int lds_bytes;     // dynamic LDS per workgroup
   size_t ws_bytes;   // workspace bytes required
 };
 
-constexpr int kLutMaxM = 16;          // M <= 16 takes the lookup-table path
+constexpr int kLutMaxM = 16;          // M <= 16 takes a GEMV path
 constexpr int kGemvWaves = 4;         // waves per GEMV workgroup
+constexpr int kDefaultSmallMPath = 2;  // M <= 16: 0 = lookup tables, 2 = matrix-core GEMV
 
-// Tuning override of the GEMV plan (0 = built-in choice), see sherry.h.
-void set_plan_override(int rw, int ch, int splits);
+// Tuning override of the GEMV plan (path -1 / others 0 = built-in choice),
+// see sherry.h.
+void set_plan_override(int path, int rw, int ch, int splits);
 
 GemmPlan plan_gemm(int M, int N, int K);
 
@@ -45,6 +48,7 @@ hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, f
 hipError_t launch_quantize_act(const float* x, int M, int K, int8_t* q, float* s_x,
                                hipStream_t stream);
 hipError_t launch_lut_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
+hipError_t launch_mfma_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 int mfma_gemm_grid(int M, int N);
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 

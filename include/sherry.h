@@ -104,10 +104,12 @@ sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
  *   workspace / workspace_bytes: scratch of at least
  *            sherry_workspace_bytes(M,N,K) bytes, 256-byte aligned, zero
  *            filled before first use (may be NULL when that size is 0).
- * M <= 16 runs the lookup-table GEMV (per-segment tables of the 16 pattern
- * dot products and their negations in LDS, one lookup per weight block);
- * M > 16 decodes the codes to int8 {-1,0,+1} tiles in LDS and contracts them
- * on int8 matrix cores.  Both return identical results. */
+ * M > 16 decodes the codes to int8 {-1,0,+1} and contracts them on int8
+ * matrix cores (workgroup tiles of 64 x 448 outputs).  M <= 16 runs either
+ * the lookup-table GEMV (per-segment tables of the 16 pattern dot products
+ * and their negations in LDS, one lookup per weight block and token pair) or
+ * the same decode + matrix-core contraction with the tokens padded to 16;
+ * sherry_gemm_plan reports which.  Every path returns identical results. */
 sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           const float* alpha, float* y, int64_t M, int64_t N,
                           int64_t K, void* workspace, size_t workspace_bytes,
@@ -121,7 +123,9 @@ sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,
 
 /* Launch plan sherry_gemm uses for a shape (host-only, pure; for
  * diagnostics and benchmarks).  Any output pointer may be NULL.
- *   path: 0 = lookup-table GEMV, 1 = decode + int8 matrix-core GEMM.
+ *   path: 0 = lookup-table GEMV (per-segment tables in LDS, §2.2),
+ *         1 = decode + int8 matrix-core GEMM (the M > 16 path),
+ *         2 = decode + int8 matrix-core GEMV (M <= 16).
  *   grid: workgroups per launch; block: threads per workgroup;
  *   splits: K-splits per output row group (1 = none);
  *   lds_bytes: LDS per workgroup. */
@@ -129,17 +133,21 @@ sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path,
                                int* grid, int* block, int* splits,
                                int* lds_bytes);
 
-/* Tuning knob for benchmark sweeps (host-only).  Replaces the built-in
- * launch plan of the lookup-table path for every later call in this process:
- *   rw     row tiles per workgroup: 1, 2 or 4 (the workgroup's 4 waves are
- *          rw row tiles x 4/rw waves sharing one); 0 = built-in choice.
- *   ch     k-tiles (128 inputs) per LDS table stage: 1, 2, 4 or 8, capped
- *          so one stage stays within 32 KB; 0 = built-in choice.
+/* Tuning knob for benchmark sweeps and tests (host-only).  Replaces the
+ * built-in launch plan for shapes with M <= 16 for every later call in this
+ * process (M > 16 always uses path 1):
+ *   path   -1 = built-in choice, or 0, 1, 2 as in sherry_gemm_plan.
+ *   rw     path 0: row tiles per workgroup, 1, 2 or 4 (the workgroup's 4
+ *          waves are rw row tiles x 4/rw waves sharing one);
+ *          path 2: waves per workgroup sharing its one row tile, 4, 8 or
+ *          16; 0 (or a value the path does not take) = built-in choice.
+ *   ch     path 0 only: k-tiles (128 inputs) per LDS table stage: 1, 2, 4
+ *          or 8, capped so one stage stays within 32 KB; 0 = built-in.
  *   splits K-splits per output row group; 0 = built-in choice.
  * Results do not depend on the plan.  sherry_workspace_bytes reflects the
  * override, so query it after setting one.  Not thread-safe with respect to
  * concurrent calls.  Returns SHERRY_ERR_SHAPE for an invalid value. */
-sherry_status sherry_gemm_plan_override(int rw, int ch, int splits);
+sherry_status sherry_gemm_plan_override(int path, int rw, int ch, int splits);
 
 #ifdef __cplusplus
 }

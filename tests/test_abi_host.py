@@ -50,11 +50,11 @@ def test_packed_bytes():
 
 def test_plan_dispatch_rule():
     for M in (1, 2, 3, 8, 15, 16):
-        assert bw.plan(M, 4096, 4096)["path"] == "lut_gemv"
+        assert bw.plan(M, 4096, 4096)["path"] in ("lut_gemv", "decode_mfma_gemv")
     for M in (17, 31, 512):
         assert bw.plan(M, 4096, 4096)["path"] == "decode_mfma"
     p = bw.plan(1, 4096, 4096)
-    assert p["block"] == 256 and p["grid"] >= 256
+    assert p["block"] in (256, 512, 1024) and p["grid"] >= 64
     # the workspace holds one 64-bit accumulator per output when split
     if p["splits"] > 1:
         assert bw.workspace_bytes(1, 4096, 4096) == 4096 * 8
@@ -64,14 +64,28 @@ def test_plan_dispatch_rule():
 def test_plan_override_changes_plan_and_workspace():
     try:
         base = bw.plan(1, 4096, 4096)
-        bw.plan_override(rw=2, ch=2, splits=8)
+        bw.plan_override("lut_gemv", rw=2, ch=2, splits=8)
         p = bw.plan(1, 4096, 4096)
+        assert p["path"] == "lut_gemv"
         assert p["splits"] == 8 and p["grid"] == 32 * 8
         assert bw.workspace_bytes(1, 4096, 4096) == 4096 * 8
-        bw.plan_override(splits=1)
+        bw.plan_override("lut_gemv", splits=1)
         assert bw.workspace_bytes(1, 4096, 4096) == 0
+        bw.plan_override("decode_mfma_gemv", rw=4, splits=4)
+        p = bw.plan(3, 4096, 4096)
+        assert p["path"] == "decode_mfma_gemv" and p["grid"] == 64 * 4 and p["block"] == 256
+        bw.plan_override("decode_mfma_gemv", rw=16, splits=2)
+        p = bw.plan(3, 4096, 4096)
+        assert p["grid"] == 64 * 2 and p["block"] == 1024
+        assert bw.workspace_bytes(3, 4096, 4096) == 3 * 4096 * 8
+        bw.plan_override("decode_mfma")
+        assert bw.plan(2, 4096, 4096)["path"] == "decode_mfma"
+        assert bw.workspace_bytes(2, 4096, 4096) == 0
+        assert bw.plan(40, 4096, 4096)["path"] == "decode_mfma"   # M > 16 unaffected
         with pytest.raises(bw.SherryError):
-            bw.plan_override(rw=3)
+            bw.plan_override("lut_gemv", rw=3)
+        assert bw.lib().sherry_gemm_plan_override(3, 0, 0, 0) == SHAPE
+        assert bw.lib().sherry_gemm_plan_override(-2, 0, 0, 0) == SHAPE
     finally:
         bw.plan_override()
     assert bw.plan(1, 4096, 4096) == base

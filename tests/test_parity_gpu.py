@@ -139,8 +139,52 @@ def test_gemm_lut_plans(orc, packed_cases, rw, ch, splits, M):
     q = synth.int8_uniform(M, K, seed=900 + M)
     acc = orc.gemm_i32(q.numpy(), T)
     try:
-        bw.plan_override(rw, ch, splits)
-        _say(f"plan override rw={rw} ch={ch} splits={splits} M={M}: {bw.plan(M, N, K)}")
+        bw.plan_override("lut_gemv", rw, ch, splits)
+        _say(f"plan override lut rw={rw} ch={ch} splits={splits} M={M}: {bw.plan(M, N, K)}")
+        gacc = bw.gemm_i32(q.cuda(), packed, N, K)
+        torch.cuda.synchronize()
+    finally:
+        bw.plan_override()
+    assert np.array_equal(gacc.cpu().numpy(), acc)
+
+
+GEMV_PLANS = [(4, 0), (4, 1), (4, 2), (4, 3), (4, 9), (8, 0), (8, 1), (8, 2), (16, 0), (16, 1),
+              (16, 5)]
+
+
+@pytest.mark.parametrize("rw,splits", GEMV_PLANS)
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 13, 16])
+@pytest.mark.parametrize("N,K", [(320, 1152), (64, 128)])
+def test_gemm_mfma_gemv_plans(orc, packed_cases, rw, splits, M, N, K):
+    """Every launch shape of the small-M matrix-core GEMV (waves per row tile
+    incl. idle ones, K-splits incl. ragged ones) gives the same exact result,
+    and the fp32 output matches the oracle."""
+    T, alpha, packed, galpha = packed_cases[(N, K)]
+    q = synth.int8_uniform(M, K, seed=1900 + M + K)
+    s_x = (torch.rand(M, generator=torch.Generator().manual_seed(M + 7)) * 0.05 + 0.001).float()
+    acc, y = orc.gemm(q.numpy(), s_x.numpy(), T, alpha)
+    try:
+        bw.plan_override("decode_mfma_gemv", rw, 0, splits)
+        _say(f"plan override gemv rw={rw} splits={splits} M={M} N={N} K={K}: {bw.plan(M, N, K)}")
+        gacc = bw.gemm_i32(q.cuda(), packed, N, K)
+        gy = bw.gemm(q.cuda(), s_x.cuda(), packed, galpha, N, K)
+        torch.cuda.synchronize()
+    finally:
+        bw.plan_override()
+    assert np.array_equal(gacc.cpu().numpy(), acc)
+    assert_y_close(gy.cpu().numpy(), y)
+
+
+@pytest.mark.parametrize("M", [1, 7, 16])
+def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M):
+    """The M > 16 kernel forced onto a small M (rows past M clamped)."""
+    N, K = 320, 1152
+    T, alpha, packed, galpha = packed_cases[(N, K)]
+    q = synth.int8_uniform(M, K, seed=2900 + M)
+    acc = orc.gemm_i32(q.numpy(), T)
+    try:
+        bw.plan_override("decode_mfma")
+        assert bw.plan(M, N, K)["path"] == "decode_mfma"
         gacc = bw.gemm_i32(q.cuda(), packed, N, K)
         torch.cuda.synchronize()
     finally:
@@ -186,13 +230,23 @@ def _workload_check(orc, name, sample_rows=None):
     torch.cuda.synchronize()
     assert np.array_equal(gq.cpu().numpy(), q), "q"
     assert np.array_equal(gs.cpu().numpy().view(np.uint32), s.view(np.uint32)), "s_x"
-    gacc = bw.gemm_i32(gq, packed, w.N, w.K).cpu().numpy()
-    gy = bw.gemm(gq, gs, packed, galpha, w.N, w.K).cpu().numpy()
     if sample_rows is None:
         acc, y = orc.gemm(q, s, T, alpha)
-        assert np.array_equal(gacc, acc), "acc"
-        assert_y_close(gy, y)
+        # every small-M path on the same inputs
+        paths = ["lut_gemv", "decode_mfma_gemv"] if w.M <= 16 else [None]
+        for path in paths:
+            try:
+                bw.plan_override(path)
+                _say(f"  path {path}: {bw.plan(w.M, w.N, w.K)}")
+                gacc = bw.gemm_i32(gq, packed, w.N, w.K).cpu().numpy()
+                gy = bw.gemm(gq, gs, packed, galpha, w.N, w.K).cpu().numpy()
+            finally:
+                bw.plan_override()
+            assert np.array_equal(gacc, acc), f"acc ({path})"
+            assert_y_close(gy, y)
     else:
+        gacc = bw.gemm_i32(gq, packed, w.N, w.K).cpu().numpy()
+        gy = bw.gemm(gq, gs, packed, galpha, w.N, w.K).cpu().numpy()
         rows = sample_rows
         acc = orc.gemm_i32(q, np.ascontiguousarray(T[rows]))
         y = orc.epilogue(acc, s, np.ascontiguousarray(alpha[rows]))
