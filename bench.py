@@ -3,8 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2a]
 
 A step is one pass of the hot path over one batch of synthetic input:
-per-token int8 quantization of the activations (sherry_quantize_act) and the
-product with the packed weights (sherry_gemm).  Offline packing
+per-token int8 quantization of the fp32 activations and the product with the
+packed weights, as one sherry_linear call (for the default workload the
+quantization runs inside the product kernel; sherry_quantize_act and
+sherry_gemm are also timed on their own).  Offline packing
 (sherry_quantize_pack) is timed separately and reported under "offline".
 Steps rotate over R copies of the packed weights whose total size exceeds
 twice the 256 MB last-level cache, so every step streams its weights from
@@ -93,11 +95,14 @@ class Setup:
         self.y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
         self.ws = torch.zeros(max(bw.workspace_bytes(w.M, w.N, w.K), 256), dtype=torch.uint8,
                               device="cuda")
+        self.scratch = torch.empty(max(bw.linear_scratch_bytes(w.M, w.N, w.K), 256),
+                                   dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
 
     def step(self, bw, i: int):
-        q, s = bw.quantize_act(self.x)
-        return self.gemm(bw, i, q, s)
+        r = i % self.R
+        return bw.linear(self.x, self.packed[r], self.alpha[r], self.w.N, self.w.K, out=self.y,
+                         workspace=self.ws, scratch=self.scratch)
 
     def gemm(self, bw, i: int, q=None, s=None):
         r = i % self.R
@@ -293,7 +298,9 @@ def main():
         "config": {"workload": "decode GEMV, LLaMA-7B attention projection (3:4 ternary W, "
                                "per-token int8 x)",
                    "M": w.M, "K": w.K, "N": w.N, "weights": f"Normal(0,{w.w_std})",
-                   "rotating_copies": st.R, "step": "sherry_quantize_act + sherry_gemm",
+                   "rotating_copies": st.R,
+                   "step": "sherry_linear (per-token int8 quantization + product)",
+                   "linear_fused": bw.linear_scratch_bytes(w.M, w.N, w.K) == 0,
                    "plan": bw.plan(w.M, w.N, w.K), "parallelism": "none (1 GPU)"},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "SherryError", "lib", "packed_bytes", "workspace_bytes", "plan", "plan_override",
-    "quantize_pack", "quantize_act", "gemm", "gemm_i32", "linear",
+    "quantize_pack", "quantize_act", "gemm", "gemm_i32", "linear", "linear_scratch_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
                 "sherry_quantize_act": ([vp, i64, i64, vp, vp, vp], ci),
                 "sherry_gemm": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
                 "sherry_gemm_i32": ([vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
+                "sherry_linear_scratch_bytes": ([i64, i64, i64], sz),
+                "sherry_linear": ([vp, vp, vp, vp, i64, i64, i64, vp, sz, vp, sz, vp], ci),
             }
             for name, (args, res) in sigs.items():
                 fn = getattr(L, name)
@@ -232,7 +234,43 @@ def gemm_i32(x: torch.Tensor, packed: torch.Tensor, N: int, K: int,
     return out
 
 
-def linear(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, N: int, K: int):
-    """fp32 activations [M,K] -> y [M,N]: per-token int8 quantization then the product."""
-    q, s = quantize_act(x)
-    return gemm(q, s, packed, alpha, N, K)
+def linear_scratch_bytes(M: int, N: int, K: int) -> int:
+    """Scratch bytes (q and s_x, any content) sherry_linear needs beyond the
+    workspace; 0 when the quantization is fused into the product."""
+    return int(lib().sherry_linear_scratch_bytes(M, N, K))
+
+
+_scratch = {}
+
+
+def linear(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, N: int, K: int,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+           scratch: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 activations [M,K] -> y [M,N]: per-token int8 quantization and the
+    product in one call (sherry_linear; fused into one kernel for small M)."""
+    px = _dev_tensor(x, "x", torch.float32)
+    _dev_tensor(packed, "packed", torch.uint8)
+    _dev_tensor(alpha, "alpha", torch.float32)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise RuntimeError(f"x must be [M,{K}]")
+    if packed.numel() != packed_bytes(N, K):
+        raise RuntimeError("packed has the wrong size for [N,K]")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    py = _dev_tensor(out, "out", torch.float32)
+    ws = workspace if workspace is not None else _workspaces.get(x.device, workspace_bytes(M, N, K))
+    nsc = linear_scratch_bytes(M, N, K)
+    if scratch is None and nsc > 0:
+        key = (x.device.index, torch.cuda.current_stream(x.device).cuda_stream)
+        scratch = _scratch.get(key)
+        if scratch is None or scratch.numel() < nsc:
+            scratch = torch.empty(max(nsc, 1 << 20), dtype=torch.uint8, device=x.device)
+            _scratch[key] = scratch
+    wp = ws.data_ptr() if ws is not None else None
+    wn = ws.numel() if ws is not None else 0
+    sp = scratch.data_ptr() if scratch is not None else None
+    sn = scratch.numel() if scratch is not None else 0
+    _check(lib().sherry_linear(px, packed.data_ptr(), alpha.data_ptr(), py, M, N, K, wp, wn, sp, sn,
+                               _stream(x.device)), "sherry_linear")
+    return out

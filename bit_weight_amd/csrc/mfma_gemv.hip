@@ -30,6 +30,12 @@
 //    product does not see).  Loaded straight from global memory through a
 //    buffer descriptor whose range ends at token M, so the padding tokens
 //    read as zero without a branch.
+//  * Fused form (FQ): the activations arrive as fp32.  Every workgroup reads
+//    its tokens' whole rows once for the per-token scale s = max|x| / 127
+//    (the same arithmetic as the stand-alone quantizer, so q and s are
+//    bit-identical to it), quantizes the k-tiles of its K-split into LDS and
+//    reads the A operands from there; this saves the quantizer's launch and
+//    its round trip through memory on the decode path.
 //  * Codes and activations are prefetched four k-tiles ahead into four
 //    register stages used in turn, so each wave keeps ~5 KB of its codes in
 //    flight (HBM streaming needs bytes in flight x latency to cover the
@@ -74,12 +80,22 @@ __device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2
   out[3] = t23[1];
 }
 
+__device__ __forceinline__ float amax4(const float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
 // KW waves share one row tile; MT = the token count rounded up to a power
-// of two (1..16).
-template <int KW, int MT>
+// of two (1..16); FQ = fused activation quantization (MT <= 4).
+template <int KW, int MT, bool FQ>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int splits, int kt_per_split) {
+  constexpr int NT = 64 * KW;
+  constexpr int QS = FQ ? kFuseMaxSpan * kTileK : 16;   // int8 activations per token in LDS
   __shared__ __attribute__((aligned(16))) uint2 dec2[1024];
   __shared__ __attribute__((aligned(16))) int red[KW * MT * kRedLd];   // [wave][token][row]
+  // [token][k in split] int8, held as 32-bit words: written and read only as
+  // 32-bit lanes, so no access reinterprets another type's storage
+  __shared__ __attribute__((aligned(16))) uint32_t qs[FQ ? MT * QS / 4 : 4];
+  __shared__ float sred[FQ ? KW * MT + MT : 1];                          // partial maxima, scales
 
   const int M = a.M, N = a.N, K = a.K, KT = K / kTileK;
   const int rt = blockIdx.x / splits;
@@ -110,8 +126,13 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
     const int ks = kt * kTileBytes, ka = kt * kTileK;
     w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
     h = __builtin_amdgcn_raw_buffer_load_b32(rc, kTileHiOff + 4 * lane, ks, 0);
-    x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka, 0, 0);
-    x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka + 16, 0, 0);
+    if constexpr (!FQ) {
+      x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka, 0, 0);
+      x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka + 16, 0, 0);
+    } else {
+      x0 = v4u{0u, 0u, 0u, 0u};
+      x1 = v4u{0u, 0u, 0u, 0u};
+    }
   };
 
   v4i acc[kBlk];
@@ -132,6 +153,49 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
     }
   }
   for (int i = tid; i < 1024; i += 64 * KW) dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
+  if constexpr (FQ) {
+    // per-token scale over the whole row (every workgroup reads its tokens'
+    // rows; four loads in flight per thread per round)
+    const int K4 = K / 4;
+    float am[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      am[m] = 0.0f;
+      if (m < M) {
+        const float4* xr = reinterpret_cast<const float4*>(a.xf + (size_t)m * K);
+#pragma unroll 4
+        for (int e = tid; e < K4; e += NT) am[m] = fmaxf(am[m], amax4(xr[e]));
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) am[m] = fmaxf(am[m], __shfl_xor(am[m], off, 64));
+      if (lane == 0) sred[q * MT + m] = am[m];
+    }
+    __syncthreads();
+    if (tid < MT) {
+      float v = 0.0f;
+#pragma unroll
+      for (int qq = 0; qq < KW; ++qq) v = fmaxf(v, sred[qq * MT + tid]);
+      sred[KW * MT + tid] = v > 0.0f ? v / 127.0f : 1.0f;   // s = max|x| / 127; a zero row -> 1
+    }
+    __syncthreads();
+    // quantize this split's k-tiles of every token into LDS: q = clamp(rint(x / s))
+    const int n4 = span * (kTileK / 4);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < M) {
+        const float sm = sred[KW * MT + m];
+        const float4* xr = reinterpret_cast<const float4*>(a.xf + (size_t)m * K + (size_t)kt_begin * kTileK);
+        for (int e = tid; e < n4; e += NT) {
+          const float4 v = xr[e];
+          const uint32_t b0 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.x / sm), -127.0f), 127.0f);
+          const uint32_t b1 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.y / sm), -127.0f), 127.0f);
+          const uint32_t b2 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.z / sm), -127.0f), 127.0f);
+          const uint32_t b3 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.w / sm), -127.0f), 127.0f);
+          qs[(m * QS) / 4 + e] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+      }
+    }
+  }
   lds_barrier();
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
 
@@ -147,7 +211,19 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
       f0[t] = v;
       f1[t] = __builtin_amdgcn_alignbit(hi[t] >> sh, v, 20);
     }
-    const v4i a0 = __builtin_bit_cast(v4i, x0), a1 = __builtin_bit_cast(v4i, x1);
+    v4i a0, a1;
+    if constexpr (FQ) {
+      // token l16 (zero past M), inputs 32g + 16s of this wave's i-th k-tile
+      const uint32_t* src = &qs[(min(l16, M - 1) * QS + (q + KW * i) * kTileK + 32 * g) / 4];
+      const v4i v0 = __builtin_bit_cast(v4i, *reinterpret_cast<const v4u*>(src));
+      const v4i v1 = __builtin_bit_cast(v4i, *reinterpret_cast<const v4u*>(src + 4));
+      const v4i z{0, 0, 0, 0};
+      a0 = l16 < M ? v0 : z;
+      a1 = l16 < M ? v1 : z;
+    } else {
+      a0 = __builtin_bit_cast(v4i, x0);
+      a1 = __builtin_bit_cast(v4i, x1);
+    }
     load(i + kStages, w, h, x0, x1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -221,7 +297,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
     const int m = q * TPW + i;
     if (m >= M || !last[i]) continue;
     if (a.y) {
-      const float tv = (float)total[i] * a.s_x[m];
+      const float tv = (float)total[i] * (FQ ? sred[KW * MT + m] : a.s_x[m]);
       a.y[(size_t)m * N + n] = tv * al;
     } else {
       a.acc[(size_t)m * N + n] = total[i];
@@ -229,27 +305,43 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   }
 }
 
-template <int KW>
+template <int KW, bool FQ>
 hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(p.grid), block(64 * KW);
-  if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1, FQ>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2, FQ>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4, FQ>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if constexpr (!FQ) {
+    if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8, false>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, false>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+template <bool FQ>
+hipError_t launch_fq(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  switch (p.rw) {
+    case 4: return launch_kw<4, FQ>(p, a, stream);
+    case 8: return launch_kw<8, FQ>(p, a, stream);
+    case 16: return launch_kw<16, FQ>(p, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
+// The fused form takes up to kFuseMaxM tokens whose rows (M*K fp32) every
+// workgroup reads once, and K-splits of at most kFuseMaxSpan k-tiles.
+bool mfma_gemv_fusable(const GemmPlan& p, int M, int K) {
+  return p.path == 2 && M <= kFuseMaxM && (long long)M * K <= kFuseMaxMK &&
+         p.kt_per_split <= kFuseMaxSpan;
+}
+
 // plan.rw carries the waves per row tile for this path (4, 8 or 16).
 hipError_t launch_mfma_gemv(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  switch (p.rw) {
-    case 4: return launch_kw<4>(p, a, stream);
-    case 8: return launch_kw<8>(p, a, stream);
-    case 16: return launch_kw<16>(p, a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return a.xf ? launch_fq<true>(p, a, stream) : launch_fq<false>(p, a, stream);
 }
 
 }  // namespace sherry

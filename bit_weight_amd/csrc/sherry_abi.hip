@@ -187,6 +187,18 @@ sherry_status run_gemm(const int8_t* x, const float* s_x, const void* packed, co
   return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
 }
 
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Scratch of sherry_linear: q [M,K] and s_x [M] when the quantization is
+// not fused into the product (any content; not kept zero).
+size_t linear_scratch(int M, int N, int K, GemmPlan* plan_out, bool* fused_out) {
+  const GemmPlan plan = plan_gemm(M, N, K);
+  const bool fused = mfma_gemv_fusable(plan, M, K);
+  if (plan_out) *plan_out = plan;
+  if (fused_out) *fused_out = fused;
+  return fused ? 0 : round256((size_t)M * K) + round256((size_t)M * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -270,6 +282,60 @@ sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,
   if (!acc) return SHERRY_ERR_NULL;
   return run_gemm(x, nullptr, packed, nullptr, nullptr, acc, M, N, K, workspace, workspace_bytes,
                   stream);
+}
+
+size_t sherry_linear_scratch_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!shape_ok(M, N, K)) return 0;
+  return linear_scratch((int)M, (int)N, (int)K, nullptr, nullptr);
+}
+
+sherry_status sherry_linear(const float* x, const void* packed, const float* alpha, float* y,
+                            int64_t M, int64_t N, int64_t K, void* workspace,
+                            size_t workspace_bytes, void* scratch, size_t scratch_bytes,
+                            void* stream) {
+  if (!x || !packed || !alpha || !y) return SHERRY_ERR_NULL;
+  if (!shape_ok(M, N, K)) return SHERRY_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(alpha, 4) || !aligned(y, 4))
+    return SHERRY_ERR_ALIGN;
+  GemmPlan plan;
+  bool fused = false;
+  const size_t need_scratch = linear_scratch((int)M, (int)N, (int)K, &plan, &fused);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return SHERRY_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SHERRY_ERR_ALIGN;
+  }
+  if (need_scratch > 0) {
+    if (!scratch || scratch_bytes < need_scratch) return SHERRY_ERR_WORKSPACE;
+    if (!aligned(scratch, 256)) return SHERRY_ERR_ALIGN;
+  }
+  const sherry_status d = check_device();
+  if (d != SHERRY_OK) return d;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  GemmArgs args{};
+  args.packed = static_cast<const uint8_t*>(packed);
+  args.alpha = alpha;
+  args.y = y;
+  args.M = (int)M;
+  args.N = (int)N;
+  args.K = (int)K;
+  if (plan.ws_bytes > 0) args.partials = static_cast<int32_t*>(workspace);
+  hipError_t e;
+  if (fused) {
+    args.xf = x;
+    e = launch_mfma_gemv(plan, args, st);
+  } else {
+    int8_t* q = static_cast<int8_t*>(scratch);
+    float* s_x = reinterpret_cast<float*>(q + round256((size_t)M * K));
+    e = launch_quantize_act(x, (int)M, (int)K, q, s_x, st);
+    if (e == hipSuccess) {
+      args.x = q;
+      args.s_x = s_x;
+      e = plan.path == 0   ? launch_lut_gemv(plan, args, st)
+          : plan.path == 2 ? launch_mfma_gemv(plan, args, st)
+                           : launch_mfma_gemm(plan, args, st);
+    }
+  }
+  return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
 }
 
 }  // extern "C"

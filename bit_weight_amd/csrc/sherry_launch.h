@@ -25,6 +25,9 @@ struct GemmPlan {
 constexpr int kLutMaxM = 16;          // M <= 16 takes a GEMV path
 constexpr int kGemvWaves = 4;         // waves per GEMV workgroup
 constexpr int kDefaultSmallMPath = 2;  // M <= 16: 0 = lookup tables, 2 = matrix-core GEMV
+constexpr int kFuseMaxM = 4;           // fused quantization: at most 4 tokens,
+constexpr int kFuseMaxMK = 16384;      //   M*K elements read per workgroup for the scales,
+constexpr int kFuseMaxSpan = 32;       //   and k-tiles per K-split held in LDS as int8
 
 // Tuning override of the GEMV plan (path -1 / others 0 = built-in choice),
 // see sherry.h.
@@ -33,7 +36,8 @@ void set_plan_override(int path, int rw, int ch, int splits);
 GemmPlan plan_gemm(int M, int N, int K);
 
 struct GemmArgs {
-  const int8_t* x;
+  const int8_t* x;     // int8 activations [M,K], or
+  const float* xf;     // fp32 activations quantized in the kernel (fused form; x unused)
   const float* s_x;
   const uint8_t* packed;
   const float* alpha;
@@ -49,6 +53,7 @@ hipError_t launch_quantize_act(const float* x, int M, int K, int8_t* q, float* s
                                hipStream_t stream);
 hipError_t launch_lut_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 hipError_t launch_mfma_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
+bool mfma_gemv_fusable(const GemmPlan& plan, int M, int K);
 int mfma_gemm_grid(int M, int N);
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 

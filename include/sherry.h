@@ -121,6 +121,29 @@ sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,
                               int64_t M, int64_t N, int64_t K, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Bytes of scratch (beyond the workspace) that sherry_linear needs for this
+ * shape: q [M,K] and s_x [M] when the quantization is not fused into the
+ * product, else 0.  Host-only, pure; 0 for an unsupported shape. */
+size_t sherry_linear_scratch_bytes(int64_t M, int64_t N, int64_t K);
+
+/* The whole decode step from fp32 activations: per-token int8 quantization
+ * (as sherry_quantize_act) followed by the product (as sherry_gemm), with
+ * identical results: y is bit-identical to calling the two.  Small token
+ * counts (M <= 4, M*K <= 16384) on the matrix-core GEMV path quantize inside
+ * the product kernel (one launch, no round trip of q through memory);
+ * otherwise q and s_x are first written to `scratch`.
+ *   x        [M,K] fp32, finite, 16-byte aligned.
+ *   packed, alpha, y, M, N, K: as sherry_gemm.
+ *   workspace / workspace_bytes: as sherry_gemm (sherry_workspace_bytes,
+ *            zero filled before first use, left zero by every call).
+ *   scratch / scratch_bytes: at least sherry_linear_scratch_bytes(M,N,K)
+ *            bytes, 256-byte aligned, any content (may be NULL when 0);
+ *            must not overlap the workspace. */
+sherry_status sherry_linear(const float* x, const void* packed, const float* alpha,
+                            float* y, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes,
+                            void* scratch, size_t scratch_bytes, void* stream);
+
 /* Launch plan sherry_gemm uses for a shape (host-only, pure; for
  * diagnostics and benchmarks).  Any output pointer may be NULL.
  *   path: 0 = lookup-table GEMV (per-segment tables in LDS, §2.2),

@@ -146,3 +146,30 @@ def test_python_wrapper_rejects_cpu_and_noncontiguous():
         bw.quantize_pack(torch.zeros(64, 128))
     with pytest.raises(RuntimeError):
         bw.quantize_act(torch.zeros(1, 128))
+
+
+def test_linear_scratch_and_validation():
+    L = bw.lib()
+    # fused (M <= 4, M*K <= 16384): no scratch
+    assert bw.linear_scratch_bytes(1, 4096, 4096) == 0
+    # not fused: q [M,K] + s_x [M], each rounded up to 256 bytes
+    assert bw.linear_scratch_bytes(16, 4096, 4096) == 16 * 4096 + 256
+    assert bw.linear_scratch_bytes(512, 14336, 4096) == 512 * 4096 + 2048
+    assert bw.linear_scratch_bytes(1, 64, 100) == 0
+    base = dict(x=FAKE, p=FAKE, al=FAKE, y=FAKE, M=1, N=64, K=128, ws=FAKE, wsb=1 << 30,
+                sc=FAKE, scb=1 << 30, st=None)
+    args = lambda **kw: [kw.get(k, v) for k, v in base.items()]
+    for k in ("x", "p", "al", "y"):
+        assert L.sherry_linear(*args(**{k: None})) == NULL, k
+    assert L.sherry_linear(*args(K=100)) == SHAPE
+    assert L.sherry_linear(*args(N=96)) == SHAPE
+    assert L.sherry_linear(*args(x=FAKE + 4)) == ALIGN
+    assert L.sherry_linear(*args(p=FAKE + 8)) == ALIGN
+    M, N, K = 16, 4096, 4096
+    need_ws, need_sc = bw.workspace_bytes(M, N, K), bw.linear_scratch_bytes(M, N, K)
+    assert need_ws > 0 and need_sc > 0
+    assert L.sherry_linear(*args(M=M, N=N, K=K, ws=None)) == WS
+    assert L.sherry_linear(*args(M=M, N=N, K=K, wsb=need_ws - 1)) == WS
+    assert L.sherry_linear(*args(M=M, N=N, K=K, sc=None)) == WS
+    assert L.sherry_linear(*args(M=M, N=N, K=K, scb=need_sc - 1)) == WS
+    assert L.sherry_linear(*args(M=M, N=N, K=K, sc=FAKE + 64)) == ALIGN

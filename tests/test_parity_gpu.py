@@ -265,3 +265,57 @@ def test_workload_5_prefill_sampled(orc):
     rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N - 1],
                                      rng.choice(w.N, 251, replace=False)]))
     _workload_check(orc, "5", sample_rows=rows)
+
+
+# ------------------------------------------- fused quantization + product
+def _linear_check(orc, x, packed, T, alpha, galpha, N, K, what):
+    q, s = orc.act_quant(x.numpy())
+    acc, y = orc.gemm(q, s, T, alpha)
+    xg = x.cuda()
+    gy = bw.linear(xg, packed, galpha, N, K)
+    gq, gs = bw.quantize_act(xg)
+    gy2 = bw.gemm(gq, gs, packed, galpha, N, K)
+    torch.cuda.synchronize()
+    # identical to quantize + product on the GPU, and to the oracle
+    assert np.array_equal(gy.cpu().numpy().view(np.uint32), gy2.cpu().numpy().view(np.uint32)), what
+    assert_y_close(gy.cpu().numpy(), y)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_linear_edges(orc, packed_cases, M, N, K):
+    T, alpha, packed, galpha = packed_cases[(N, K)]
+    x = synth.activations(M, K, seed=3100 + M + K, outlier_channels=(M % 2 == 1))
+    if M >= 3:
+        x[1] = 0.0                                   # an all-zero token
+    _say(f"linear M={M} N={N} K={K} scratch={bw.linear_scratch_bytes(M, N, K)} plan={bw.plan(M, N, K)}")
+    _linear_check(orc, x, packed, T, alpha, galpha, N, K, f"M={M}")
+
+
+@pytest.mark.parametrize("path,rw,splits", [("decode_mfma_gemv", 4, 1), ("decode_mfma_gemv", 4, 3),
+                                            ("decode_mfma_gemv", 16, 2), ("decode_mfma_gemv", 8, 9),
+                                            ("lut_gemv", 0, 0), ("decode_mfma", 0, 0)])
+@pytest.mark.parametrize("M", [1, 4])
+def test_linear_plans(orc, packed_cases, path, rw, splits, M):
+    """Fused (matrix-core GEMV) and unfused (other paths) forms agree."""
+    N, K = 320, 1152
+    T, alpha, packed, galpha = packed_cases[(N, K)]
+    x = synth.activations(M, K, seed=4100 + M, outlier_channels=True)
+    try:
+        bw.plan_override(path, rw, 0, splits)
+        _say(f"linear plan {path} rw={rw} splits={splits} M={M}: {bw.plan(M, N, K)}")
+        _linear_check(orc, x, packed, T, alpha, galpha, N, K, f"{path} {rw} {splits}")
+    finally:
+        bw.plan_override()
+
+
+@pytest.mark.parametrize("name", ["1", "2a", "2b", "2c", "3a", "3b", "4"])
+def test_linear_workloads(orc, name):
+    w = synth.WORKLOADS[name]
+    W = synth.workload_weights(w)
+    x = synth.workload_activations(w)
+    T, alpha = orc.quantize(W.numpy())
+    packed, galpha = gpu_pack(W)
+    del W
+    _say(f"linear workload {w.description} scratch={bw.linear_scratch_bytes(w.M, w.N, w.K)}")
+    _linear_check(orc, x, packed, T, alpha, galpha, w.N, w.K, name)
