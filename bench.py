@@ -16,8 +16,9 @@ HIP events (recorded on the stream the kernels run on) around the replay.
 Prints ONE JSON line.  `value` is packed-weight GB/s of the whole step
 (N*K*5/32 bytes per step / step time) on the default workload (decode GEMV,
 LLaMA-7B attention projection: M=1, K=4096, N=4096).  "roofline" is the
-dominant kernel (the product kernel the launch plan picks for that shape)
-against the 8 TB/s HBM peak; "prefill" holds the M=512 decode + int8 MFMA
+dominant kernel against the 8 TB/s HBM peak: the step's one kernel when the
+quantization is fused into the product (as it is for this workload), else
+the product kernel the launch plan picks; "prefill" holds the M=512 decode + int8 MFMA
 product against the 5.0 POP/s int8 peak; "workloads" holds every workload's
 kernel time, and for M <= 16 the time of each small-M path (lookup-table
 GEMV and matrix-core GEMV).  "cpu_baseline" times the CPU oracle (single
@@ -131,15 +132,17 @@ def graph_time(torch, fn, n: int, reps: int = 1):
     return best, g
 
 
-def algorithmic_bytes(w) -> int:
-    """Bytes a product launch must move at least: packed codes, alpha, int8 x,
-    s_x and the fp32 y."""
-    return w.packed_bytes + 4 * w.N + w.M * w.K + 4 * w.M + 4 * w.M * w.N
+def algorithmic_bytes(w, fp32_x: bool = False) -> int:
+    """Bytes a product launch must move at least: packed codes, alpha, the
+    activations (int8 x and s_x, or fp32 x for the fused form) and fp32 y."""
+    x_bytes = 4 * w.M * w.K if fp32_x else w.M * w.K + 4 * w.M
+    return w.packed_bytes + 4 * w.N + x_bytes + 4 * w.M * w.N
 
 
 KERNEL_SOURCES = {
     "lut_gemv": ("lut_gemv.hip", "sherry_device.h", "sherry_launch.h"),
     "mfma_gemv": ("mfma_gemv.hip", "sherry_device.h", "sherry_launch.h"),
+    "mfma_gemv_fused": ("mfma_gemv.hip", "sherry_device.h", "sherry_launch.h"),
     "mfma_gemm": ("mfma_gemm.hip", "sherry_device.h", "sherry_launch.h"),
 }
 # plan path -> kernel tag
@@ -235,8 +238,10 @@ def main():
             st = Setup(torch, bw, synth, name, args.copies)
             n = max(args.steps, st.R)
             ms, _ = graph_time(torch, lambda i: st.gemm(bw, i), n)
-            print(f"{name}: {ms * 1e3:.3f} us/launch, {st.w.packed_bytes / ms / 1e6:.1f} GB/s packed,"
-                  f" R={st.R}, plan={bw.plan(st.w.M, st.w.N, st.w.K)}", flush=True)
+            ms_l, _ = graph_time(torch, lambda i: st.step(bw, i), n)
+            print(f"{name}: sherry_gemm {ms * 1e3:.3f} us/launch, {st.w.packed_bytes / ms / 1e6:.1f} GB/s"
+                  f" packed; sherry_linear {ms_l * 1e3:.3f} us; R={st.R},"
+                  f" plan={bw.plan(st.w.M, st.w.N, st.w.K)}", flush=True)
             del st
             torch.cuda.empty_cache()
         return
@@ -276,11 +281,21 @@ def main():
     n_k = max(args.steps, st.R)
     gemm_ms, _ = graph_time(torch, lambda i: st.gemm(bw, i), n_k, reps=3)
     act_ms, _ = graph_time(torch, lambda i: bw.quantize_act(st.x), n_k, reps=3)
-    alg = algorithmic_bytes(w)
-    achieved = alg / gemm_ms / 1e6
     plan = bw.plan(w.M, w.N, w.K)
     kern = PATH_KERNEL[plan["path"]]
-    traffic = traffic_from_profile(kern, name, plan)
+    fused = bw.linear_scratch_bytes(w.M, w.N, w.K) == 0
+    if fused:
+        # the step is one kernel (quantization fused into the product): its
+        # duration is the timed region's per-step time, and its algorithmic
+        # bytes read the fp32 activations
+        alg = algorithmic_bytes(w, fp32_x=True)
+        kern_ms = step_ms
+        traffic = traffic_from_profile(kern + "_fused", name, plan)
+    else:
+        alg = algorithmic_bytes(w)
+        kern_ms = gemm_ms
+        traffic = traffic_from_profile(kern, name, plan)
+    achieved = alg / kern_ms / 1e6
     value = w.packed_bytes / step_ms / 1e6
     out = {
         "metric": METRIC,
@@ -305,8 +320,9 @@ def main():
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": f"{kern}_kernel",
-                     "kernel_us": round(gemm_ms * 1e3, 3), "bytes_per_launch": alg,
+                     "traffic": traffic,
+                     "kernel": f"{kern}_kernel" + (" (fused quantization)" if fused else ""),
+                     "kernel_us": round(kern_ms * 1e3, 3), "bytes_per_launch": alg,
                      "packed_bytes_per_launch": w.packed_bytes},
         "kernels_us": {"sherry_gemm": round(gemm_ms * 1e3, 3),
                        "sherry_quantize_act": round(act_ms * 1e3, 3)},
