@@ -6,22 +6,26 @@
 // decode-then-int8-GEMM structure the OdysseyLLM FastGEMM review describes
 // for W4A8 (xllm-io page, FastGEMM section).
 //
-// Workgroup tile: BM = 64 activation rows x BN = 448 weight rows, k-steps of
-// one format k-tile (128 inputs); 4 waves, one per SIMD.  The waves split the
-// weight rows (112 each = 7 MFMA column blocks) and share the activation
-// tile, so each wave owns 64 x 112 outputs (4 x 7 blocks of 16 x 16):
-//  * activations: 64 x 128 int8 per k-step, loaded once per workgroup into a
+// Workgroup tile: BM = 128 activation rows x BN = 256 weight rows (4 format
+// row tiles), k-steps of one format k-tile (128 inputs); 4 waves, one per
+// SIMD.  Wave w owns row tile w, i.e. 64 weight rows = 4 MFMA column blocks,
+// against all 128 activation rows = 8 MFMA row blocks (8 x 4 accumulators).
+// A decoded weight operand therefore feeds 8 MFMAs and an activation
+// fragment 4, which keeps the LDS work per k-tile (pair-table lookups plus
+// activation fragments) well below the matrix-core time.
+//  * activations: 128 x 128 int8 per k-step, loaded once per workgroup into a
 //    double-buffered, chunk-major LDS tile (see a_slot), read as MFMA A
 //    operands (16 bytes per lane) without bank conflicts;
-//  * weights: each wave decodes exactly the B operands it consumes.  Lane l
-//    of a 16-column block holds weight row l%16; lane group g = l/16 takes
-//    codes 8g..8g+7 of the k-tile (inputs 32g..32g+31: the first half in
-//    MFMA sub-step 0, the second in sub-step 1).  The A operands use the
-//    same input order, which a dot product does not see.  Those 40 code bits
-//    always lie in two dwords of the row's 160-bit string, so a lane loads
-//    2 dwords per row; a 1024-entry LDS table maps a 10-bit code pair to its
-//    8 int8 weights, so 4 codes cost two 8-byte lookups and four VALU ops.
-//    No decoded weight is written to LDS or decoded twice in a workgroup;
+//  * weights: each wave decodes exactly the B operands it consumes.  It loads
+//    its row tile's 1280-byte k-tile coalesced (lane r = tile row r, 16 + 4
+//    bytes) and moves dwords g and g+1 of rows 16t..16t+15 to lane group g of
+//    column block t with two 4 x 4 transposes of 16-lane rows
+//    (v_permlane32_swap, then v_permlane16_swap).  Lane l of a block then
+//    holds weight row l%16 and, for lane group g = l/16, codes 8g..8g+7 of
+//    the k-tile (inputs 32g..32g+31: the first half in MFMA sub-step 0, the
+//    second in sub-step 1); the A operands use the same input order, which a
+//    dot product does not see.  A 1024-entry LDS table maps a 10-bit code
+//    pair to its 8 int8 weights, so 4 codes cost two 8-byte lookups;
 //  * codes and activations come through buffer descriptors (32-bit lane
 //    offsets, scalar k-step offset) two k-steps ahead into two register
 //    stages used in turn; the barrier orders LDS only, so the prefetched
@@ -38,27 +42,42 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 64, kBN = 448, kWN = kBN / 4, kNT = kWN / 16;  // 7 column blocks / wave
-constexpr int kMT = kBM / 16;                                      // 4 row blocks / wave
-constexpr int kBK = kTileK;                                        // 128
-constexpr int kChunks = kBK / 16;                                  // 16-byte input chunks
-constexpr int kAStage = kBM * kBK;                                 // 8 KB per k-step
-constexpr int kOutLd = kBN + 4;          // floats per row of the epilogue tile (+16 B pad)
-constexpr int kLdsMain = 2 * kAStage + 8192;     // activation stages + pair table
-constexpr int kLdsOut = 16 * kOutLd * 4;         // epilogue tile
+constexpr int kBM = 128, kBN = 256;             // workgroup tile
+constexpr int kMT = kBM / 16;                   // 8 row blocks per wave
+constexpr int kNT = kTileRows / 16;             // 4 column blocks per wave (one row tile)
+constexpr int kBK = kTileK;                     // 128
+constexpr int kAStage = kBM * kBK;              // 16 KB per k-step
+constexpr int kAPerThread = kAStage / 16 / 256; // 16-byte chunks each thread stages (4)
+constexpr int kOutLd = kBN + 4;                 // words per row of the epilogue tile (+16 B)
+constexpr int kLdsMain = 2 * kAStage + 8192;    // activation stages + pair table
+constexpr int kLdsOut = 16 * kOutLd * 4;        // epilogue tile (16 rows)
 constexpr int kLdsBytes = kLdsMain > kLdsOut ? kLdsMain : kLdsOut;
 
 // Activation tile in LDS, chunk-major: the 16-byte chunk c of row r sits at
-// slot c * 64 + (r ^ c).  A wave's fragment read (16 consecutive rows, one
+// slot c * kBM + (r ^ c).  A wave's fragment read (16 consecutive rows, one
 // chunk) covers 256 contiguous bytes, and a row-contiguous write (8 lanes,
 // one row, chunks 0..7) hits 8 different bank groups.
 __device__ __forceinline__ int a_slot(int r, int c) { return (c * kBM + (r ^ c)) * 16; }
 
-// One MFMA sub-step: decode 4 codes per row into B operands (two 10-bit
-// code pairs, one 8-byte table entry each), then 4 x 7 MFMAs.
-__device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const uint32_t (&f)[kNT],
-                                        const int8_t* as, int l16, int c, const uint8_t* dec2) {
-  v4i bop[kNT];
+// 4 x 4 transpose of 16-lane rows: out[t] row g = in[g] row t.
+__device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                           uint32_t (&out)[4]) {
+  // swap the upper 32 lanes of the first operand with the lower 32 of the second
+  const auto s02 = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+  // swap the odd 16-lane rows of the first operand with the even rows of the second
+  const auto t01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  const auto t23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  out[0] = t01[0];
+  out[1] = t01[1];
+  out[2] = t23[0];
+  out[3] = t23[1];
+}
+
+// Decode of one MFMA sub-step: 4 codes per row into B operands (two 10-bit
+// code pairs, one 8-byte table entry each).
+__device__ __forceinline__ void mg_decode(v4i (&bop)[kNT], const uint32_t (&f)[kNT],
+                                          const uint8_t* dec2) {
 #pragma unroll
   for (int t = 0; t < kNT; ++t) {
     const uint32_t v = f[t];
@@ -66,12 +85,32 @@ __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const uint32_t (&f
     const uint2 e1 = *reinterpret_cast<const uint2*>(dec2 + ((v >> 7) & 0x1FF8u));
     bop[t] = v4i{(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
   }
+}
+
+// The 8 x 4 MFMAs of one sub-step (A chunk c of the k-step tile at `as`).
+// The A fragments of the next two row blocks are requested before the
+// MFMAs of the current two, so the LDS latency hides behind 8 MFMAs.
+__device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&bop)[kNT],
+                                        const int8_t* as, int l16, int c) {
+  auto frag = [&](int i) { return *reinterpret_cast<const v4i*>(as + a_slot(16 * i + l16, c)); };
+  v4i a0 = frag(0), a1 = frag(1);
 #pragma unroll
-  for (int i = 0; i < kMT; ++i) {
-    const v4i aop = *reinterpret_cast<const v4i*>(as + a_slot(16 * i + l16, c));
+  for (int i = 0; i < kMT; i += 2) {
+    v4i n0 = a0, n1 = a1;
+    if (i + 2 < kMT) {
+      n0 = frag(i + 2);
+      n1 = frag(i + 3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
-      acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop[t], acc[i][t], 0, 0, 0);
+      acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bop[t], acc[i][t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
+      acc[i + 1][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bop[t], acc[i + 1][t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    a0 = n0;
+    a1 = n1;
   }
 }
 
@@ -88,7 +127,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
   int8_t (*As)[kAStage] = reinterpret_cast<int8_t (*)[kAStage]>(lds);
   uint2* dec2 = reinterpret_cast<uint2*>(lds + 2 * kAStage / 4);
 
-  const int M = a.M, N = a.N, K = a.K, KT = K / kTileK;
+  const int M = a.M, N = a.N, K = a.K, KT = K / kTileK, RT = N / kTileRows;
   // tile id -> (m tile, n tile): consecutive ids of one XCD share n tiles
   const int id = blockIdx.x;
   const int mt_count = (M + kBM - 1) / kBM;
@@ -99,49 +138,30 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
   const int nt_idx = xcd * per_xcd + owned;
   if (nt_idx >= n_tiles || mt_idx >= mt_count) return;  // padding ids
   const int m0 = mt_idx * kBM, n0 = nt_idx * kBN;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
 
   // decode table: code pair (c0 | c1 << 5) -> the 8 int8 weights of both
   for (int i = tid; i < 1024; i += 256) dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
 
-  // Buffer descriptors: the workgroup's first code tile row and first
-  // activation row.  Per-lane offsets are 32-bit, the k-step is a scalar
-  // offset, so a load costs no VALU work.
-  const size_t pk_base = tile_offset(n0 / kTileRows, 0, KT);
-  const size_t pk_total = (size_t)N * (size_t)K * 5 / 32;
-  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.packed + pk_base, pk_total - pk_base);
+  // This wave's row tile (N % 64 == 0, so a row tile is all valid or all
+  // past N; one past N streams the last tile and stores nothing).
+  const int rt_raw = n0 / kTileRows + wave;
+  const bool n_live = rt_raw < RT;
+  const int rt = n_live ? rt_raw : RT - 1;
+  const __amdgpu_buffer_rsrc_t rc =
+      buffer_rsrc(a.packed + tile_offset(rt, 0, KT), (size_t)KT * kTileBytes);
   const __amdgpu_buffer_rsrc_t ra =
       buffer_rsrc(a.x + (size_t)m0 * K, (size_t)(M - m0) * (size_t)K);
-
-  // this lane's weight rows (one per 16-column block)
-  int rows[kNT];
-  bool rv[kNT];
-#pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    rows[t] = n0 + wave * kWN + 16 * t + l16;
-    rv[t] = (n0 + wave * kWN + 16 * t) < N;  // N % 64 == 0: blocks are all-or-none
-  }
-  // The lane's two code dwords of a row: dword g and dword g+1 of the
-  // 160-bit string (dword 4 lives in the tile's 4-byte part).  Rows past N
-  // (whole 16-row blocks) read row N-1: their products land in columns that
-  // are never stored, so no load needs a branch.
   const uint32_t sh = 8u * (uint32_t)g;  // bit 40g mod 32
-  int lo_v[kNT], hi_v[kNT];
-#pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    const int row = rv[t] ? rows[t] : N - 1;
-    const int tb = (row / kTileRows - n0 / kTileRows) * KT * kTileBytes;
-    const int r = row % kTileRows;
-    lo_v[t] = tb + 16 * r + 4 * g;
-    hi_v[t] = tb + (g < 3 ? 16 * r + 4 * (g + 1) : kTileHiOff + 4 * r);
-  }
-  // activations: 64 rows x 128 bytes per k-step, two 16-byte chunks per
+
+  // activations: 128 rows x 128 bytes per k-step, four 16-byte chunks per
   // thread (8 lanes per row: coalesced); rows past M read row M-1 (they feed
   // only unstored output rows)
-  int a_v[2], a_lds[2];
+  int a_v[kAPerThread], a_lds[kAPerThread];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kAPerThread; ++i) {
     const int idx = tid + 256 * i, row = idx >> 3, c = idx & 7;
     a_v[i] = min(row, M - 1 - m0) * K + c * 16;
     a_lds[i] = a_slot(row, c);
@@ -153,25 +173,28 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-  // Codes and activations of k-step kt for this lane.
-  auto load = [&](int kt_, uint32_t* lo, uint32_t* hi, v4u& v0, v4u& v1) {
+  // Codes (coalesced, lane = tile row) and activations of k-step kt.
+  auto load = [&](int kt_, v4u& w, uint32_t& h, v4u (&av)[kAPerThread]) {
     const int ks = kt_ * kTileBytes, ka = kt_ * kBK;
+    w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
+    h = __builtin_amdgcn_raw_buffer_load_b32(rc, kTileHiOff + 4 * lane, ks, 0);
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-      lo[t] = __builtin_amdgcn_raw_buffer_load_b32(rc, lo_v[t], ks, 0);
-      hi[t] = __builtin_amdgcn_raw_buffer_load_b32(rc, hi_v[t], ks, 0);
-    }
-    v0 = __builtin_amdgcn_raw_buffer_load_b128(ra, a_v[0], ka, 0);
-    v1 = __builtin_amdgcn_raw_buffer_load_b128(ra, a_v[1], ka, 0);
+    for (int i = 0; i < kAPerThread; ++i)
+      av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_v[i], ka, 0);
   };
+  const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
   // One k-step from one register stage; the stage is refilled with the
   // loads for k-step kt+2 before the MFMAs.  The scheduling barriers keep
   // the refill loads inside their own step, so every step finds exactly one
   // newer stage in flight and waits only for its own.
-  auto step = [&](int kt_, uint32_t* lo, uint32_t* hi, v4u& v0, v4u& v1) {
+  auto step = [&](int kt_, v4u& w, uint32_t& h, v4u (&av)[kAPerThread]) {
     int8_t* as = &As[kt_ & 1][0];
-    *reinterpret_cast<v4u*>(as + a_lds[0]) = v0;
-    *reinterpret_cast<v4u*>(as + a_lds[1]) = v1;
+#pragma unroll
+    for (int i = 0; i < kAPerThread; ++i) *reinterpret_cast<v4u*>(as + a_lds[i]) = av[i];
+    // lane (l16, g) of block t <- dwords g (lo) and g+1 (hi) of row 16t+l16
+    uint32_t lo[kNT], hi[kNT];
+    transpose4(w.x, w.y, w.z, w.w, lo);
+    transpose4(w.y, w.z, w.w, h, hi);
     // codes 8g..8g+3 (sub-step 0) and 8g+4..8g+7 (sub-step 1), 20 bits each
     uint32_t f0[kNT], f1[kNT];
 #pragma unroll
@@ -180,40 +203,44 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
       f0[t] = x0;
       f1[t] = __builtin_amdgcn_alignbit(hi[t] >> sh, x0, 20);
     }
-    load(min(kt_ + 2, KT - 1), lo, hi, v0, v1);
+    load(min(kt_ + 2, KT - 1), w, h, av);
     __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();  // this k-step's activations are in LDS
-    mg_mfma(acc, f0, as, l16, 2 * g, reinterpret_cast<const uint8_t*>(dec2));
-    mg_mfma(acc, f1, as, l16, 2 * g + 1, reinterpret_cast<const uint8_t*>(dec2));
+    v4i bop[kNT];
+    mg_decode(bop, f0, d2);      // the table is fixed: no wait for the barrier
+    lds_barrier();               // this k-step's activations are in LDS
+    mg_mfma(acc, bop, as, l16, 2 * g);
+    mg_decode(bop, f1, d2);
+    mg_mfma(acc, bop, as, l16, 2 * g + 1);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // two register stages, ping-pong: no register copies between k-steps
-  uint32_t lo0[kNT], hi0[kNT], lo1[kNT], hi1[kNT];
-  v4u a00, a01, a10, a11;
-  load(0, lo0, hi0, a00, a01);
+  v4u w0, w1, av0[kAPerThread], av1[kAPerThread];
+  uint32_t h0, h1;
+  load(0, w0, h0, av0);
   __builtin_amdgcn_sched_barrier(0);  // stage 0's loads strictly before stage 1's
-  load(min(1, KT - 1), lo1, hi1, a10, a11);
+  load(min(1, KT - 1), w1, h1, av1);
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();  // decode table
 
   int kt = 0;
   for (; kt + 2 <= KT; kt += 2) {
-    step(kt, lo0, hi0, a00, a01);
-    step(kt + 1, lo1, hi1, a10, a11);
+    step(kt, w0, h0, av0);
+    step(kt + 1, w1, h1, av1);
   }
-  if (kt < KT) step(kt, lo0, hi0, a00, a01);
+  if (kt < KT) step(kt, w0, h0, av0);
 
-  // Epilogue, one 16-row block at a time: every wave writes its 16 x 112
+  // Epilogue, one 16-row block at a time: every wave writes its 16 x 64
   // results (y = ((float)acc * s_x[m]) * alpha[n], or the raw int32) into a
-  // row-major LDS tile of 16 x 448, then the workgroup stores whole rows,
+  // row-major LDS tile of 16 x 256, then the workgroup stores whole rows,
   // 16 bytes per lane, so each store instruction writes full 128-byte lines.
   // Lane (l16, g) of a 16 x 16 MFMA block holds column l16, rows 4g..4g+3.
   uint32_t* ot = lds;   // [16][kOutLd] result words
   const bool want_y = a.y != nullptr;
   float al[kNT];
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) al[t] = want_y && rv[t] ? a.alpha[rows[t]] : 0.0f;
+  for (int t = 0; t < kNT; ++t)
+    al[t] = want_y && n_live ? a.alpha[rt * kTileRows + 16 * t + l16] : 0.0f;
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
     __syncthreads();  // previous use of the LDS area is finished
@@ -224,7 +251,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
       const float sx = want_y ? a.s_x[m] : 0.0f;
 #pragma unroll
       for (int t = 0; t < kNT; ++t) {
-        const int col = wave * kWN + 16 * t + l16;
+        const int col = wave * kTileRows + 16 * t + l16;
         uint32_t v;
         if (want_y) {
           const float tv = (float)acc[i][t][r] * sx;
@@ -236,7 +263,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
       }
     }
     __syncthreads();
-    // 16 rows x 112 float4 per block
+    // 16 rows x 64 float4 per block
     for (int e = tid; e < 16 * (kBN / 4); e += 256) {
       const int ml = e / (kBN / 4), c4 = e - ml * (kBN / 4);
       const int m = m0 + 16 * i + ml, n = n0 + 4 * c4;

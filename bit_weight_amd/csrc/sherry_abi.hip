@@ -102,7 +102,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
     p.block = 256;
     p.splits = 1;
     p.kt_per_split = K / kTileK;
-    p.lds_bytes = 16 * (448 + 4) * 4;  // epilogue tile, the largest LDS use
+    p.lds_bytes = 2 * 128 * kTileK + 1024 * 8;  // activation stages + pair table
     p.ws_bytes = 0;
     return p;
   }
