@@ -48,8 +48,9 @@ constexpr int kNT = kTileRows / 16;             // 4 column blocks per wave (one
 constexpr int kBK = kTileK;                     // 128
 constexpr int kAStage = kBM * kBK;              // 16 KB per k-step
 constexpr int kAPerThread = kAStage / 16 / 256; // 16-byte chunks each thread stages (4)
+constexpr int kThreads = 512;                   // 4 row tiles x 2 k-tile parities
 constexpr int kOutLd = kBN + 4;                 // words per row of the epilogue tile (+16 B)
-constexpr int kLdsMain = 2 * kAStage + 8192;    // activation stages + pair table
+constexpr int kLdsMain = 4 * kAStage + 8192;    // 2 buffers x 2 parities + pair table
 constexpr int kLdsOut = 16 * kOutLd * 4;        // epilogue tile (16 rows)
 constexpr int kLdsBytes = kLdsMain > kLdsOut ? kLdsMain : kLdsOut;
 
@@ -119,13 +120,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-__global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles) {
-  // one LDS block: two activation stages, then the pair table; after the
-  // main loop the epilogue tile reuses all of it
+__global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_tiles) {
+  // one LDS block: the activation buffers [buffer][parity], then the pair
+  // table; after the main loop the epilogue tile reuses all of it
   // (32-bit words: every view below is a character type or 32-bit lanes)
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsBytes / 4];
   int8_t (*As)[kAStage] = reinterpret_cast<int8_t (*)[kAStage]>(lds);
-  uint2* dec2 = reinterpret_cast<uint2*>(lds + 2 * kAStage / 4);
+  uint2* dec2 = reinterpret_cast<uint2*>(lds + 4 * kAStage / 4);
 
   const int M = a.M, N = a.N, K = a.K, KT = K / kTileK, RT = N / kTileRows;
   // tile id -> (m tile, n tile): consecutive ids of one XCD share n tiles
@@ -139,11 +140,13 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
   if (nt_idx >= n_tiles || mt_idx >= mt_count) return;  // padding ids
   const int m0 = mt_idx * kBM, n0 = nt_idx * kBN;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wv & 3, kh = wv >> 2;            // row tile, k-tile parity
   const int l16 = lane & 15, g = lane >> 4;
 
   // decode table: code pair (c0 | c1 << 5) -> the 8 int8 weights of both
-  for (int i = tid; i < 1024; i += 256) dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
+  for (int i = tid; i < 1024; i += kThreads)
+    dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
 
   // This wave's row tile (N % 64 == 0, so a row tile is all valid or all
   // past N; one past N streams the last tile and stores nothing).
@@ -156,13 +159,13 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
       buffer_rsrc(a.x + (size_t)m0 * K, (size_t)(M - m0) * (size_t)K);
   const uint32_t sh = 8u * (uint32_t)g;  // bit 40g mod 32
 
-  // activations: 128 rows x 128 bytes per k-step, four 16-byte chunks per
-  // thread (8 lanes per row: coalesced); rows past M read row M-1 (they feed
-  // only unstored output rows)
+  // activations: each parity's 256 threads stage its k-tile, 128 rows x 128
+  // bytes, four 16-byte chunks per thread (8 lanes per row: coalesced); rows
+  // past M read row M-1 (they feed only unstored output rows)
   int a_v[kAPerThread], a_lds[kAPerThread];
 #pragma unroll
   for (int i = 0; i < kAPerThread; ++i) {
-    const int idx = tid + 256 * i, row = idx >> 3, c = idx & 7;
+    const int idx = (tid & 255) + 256 * i, row = idx >> 3, c = idx & 7;
     a_v[i] = min(row, M - 1 - m0) * K + c * 16;
     a_lds[i] = a_slot(row, c);
   }
@@ -173,8 +176,12 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-  // Codes (coalesced, lane = tile row) and activations of k-step kt.
-  auto load = [&](int kt_, v4u& w, uint32_t& h, v4u (&av)[kAPerThread]) {
+  // Codes (coalesced, lane = tile row) and activations of this wave's
+  // k-tile of pair j (2j + kh, clamped: a prefetch past the end re-reads the
+  // last k-tile).
+  const int KJ = (KT + 1) / 2;
+  auto load = [&](int j, v4u& w, uint32_t& h, v4u (&av)[kAPerThread]) {
+    const int kt_ = min(2 * j + kh, KT - 1);
     const int ks = kt_ * kTileBytes, ka = kt_ * kBK;
     w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
     h = __builtin_amdgcn_raw_buffer_load_b32(rc, kTileHiOff + 4 * lane, ks, 0);
@@ -187,8 +194,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
   // loads for k-step kt+2 before the MFMAs.  The scheduling barriers keep
   // the refill loads inside their own step, so every step finds exactly one
   // newer stage in flight and waits only for its own.
-  auto step = [&](int kt_, v4u& w, uint32_t& h, v4u (&av)[kAPerThread]) {
-    int8_t* as = &As[kt_ & 1][0];
+  auto step = [&](int j, v4u& w, uint32_t& h, v4u (&av)[kAPerThread]) {
+    int8_t* as = &As[(j & 1) * 2 + kh][0];
+    const bool live = 2 * j + kh < KT;     // odd KT: the last pair has one k-tile
 #pragma unroll
     for (int i = 0; i < kAPerThread; ++i) *reinterpret_cast<v4u*>(as + a_lds[i]) = av[i];
     // lane (l16, g) of block t <- dwords g (lo) and g+1 (hi) of row 16t+l16
@@ -203,14 +211,16 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
       f0[t] = x0;
       f1[t] = __builtin_amdgcn_alignbit(hi[t] >> sh, x0, 20);
     }
-    load(min(kt_ + 2, KT - 1), w, h, av);
+    load(min(j + 2, KJ - 1), w, h, av);
     __builtin_amdgcn_sched_barrier(0);
     v4i bop[kNT];
     mg_decode(bop, f0, d2);      // the table is fixed: no wait for the barrier
-    lds_barrier();               // this k-step's activations are in LDS
-    mg_mfma(acc, bop, as, l16, 2 * g);
-    mg_decode(bop, f1, d2);
-    mg_mfma(acc, bop, as, l16, 2 * g + 1);
+    lds_barrier();               // this pair's activations are in LDS
+    if (live) {
+      mg_mfma(acc, bop, as, l16, 2 * g);
+      mg_decode(bop, f1, d2);
+      mg_mfma(acc, bop, as, l16, 2 * g + 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -219,16 +229,16 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
   uint32_t h0, h1;
   load(0, w0, h0, av0);
   __builtin_amdgcn_sched_barrier(0);  // stage 0's loads strictly before stage 1's
-  load(min(1, KT - 1), w1, h1, av1);
+  load(min(1, KJ - 1), w1, h1, av1);
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();  // decode table
 
-  int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    step(kt, w0, h0, av0);
-    step(kt + 1, w1, h1, av1);
+  int j = 0;
+  for (; j + 2 <= KJ; j += 2) {
+    step(j, w0, h0, av0);
+    step(j + 1, w1, h1, av1);
   }
-  if (kt < KT) step(kt, w0, h0, av0);
+  if (j < KJ) step(j, w0, h0, av0);
 
   // Epilogue, one 16-row block at a time: every wave writes its 16 x 64
   // results (y = ((float)acc * s_x[m]) * alpha[n], or the raw int32) into a
@@ -244,6 +254,24 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
     __syncthreads();  // previous use of the LDS area is finished
+    // the odd-parity waves hand their int32 sums to the even ones
+    if (kh == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < kNT; ++t)
+          ot[(4 * g + r) * kOutLd + wave * kTileRows + 16 * t + l16] = (uint32_t)acc[i][t][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < kNT; ++t)
+          acc[i][t][r] += (int)ot[(4 * g + r) * kOutLd + wave * kTileRows + 16 * t + l16];
+    }
+    __syncthreads();
+    if (kh == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int ml = 4 * g + r;                 // row within the block
@@ -262,9 +290,10 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int n_tiles)
         ot[ml * kOutLd + col] = v;
       }
     }
+    }
     __syncthreads();
     // 16 rows x 64 float4 per block
-    for (int e = tid; e < 16 * (kBN / 4); e += 256) {
+    for (int e = tid; e < 16 * (kBN / 4); e += kThreads) {
       const int ml = e / (kBN / 4), c4 = e - ml * (kBN / 4);
       const int m = m0 + 16 * i + ml, n = n0 + 4 * c4;
       if (m < M && n < N) {
@@ -287,7 +316,7 @@ int mfma_gemm_grid(int M, int N) {
 
 hipError_t launch_mfma_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   const int nt = (a.N + kBN - 1) / kBN;
-  hipLaunchKernelGGL(mfma_gemm_kernel, dim3(p.grid), dim3(256), 0, stream, a, nt);
+  hipLaunchKernelGGL(mfma_gemm_kernel, dim3(p.grid), dim3(kThreads), 0, stream, a, nt);
   return hipGetLastError();
 }
 

@@ -99,10 +99,10 @@ GemmPlan plan_gemm(int M, int N, int K) {
   if (M > kLutMaxM) {
     p.path = 1;
     p.grid = mfma_gemm_grid(M, N);
-    p.block = 256;
+    p.block = 512;
     p.splits = 1;
     p.kt_per_split = K / kTileK;
-    p.lds_bytes = 2 * 128 * kTileK + 1024 * 8;  // activation stages + pair table
+    p.lds_bytes = 4 * 128 * kTileK + 1024 * 8;  // activation buffers + pair table
     p.ws_bytes = 0;
     return p;
   }
