@@ -212,6 +212,39 @@ def cpu_baseline(name: str, seconds: float):
                       f"{el:.1f} s, {per * 1e3:.2f} ms/step; host {platform.processor() or platform.machine()}"}
 
 
+def grouped_bench(torch, bw, synth):
+    """q/k/v-style group at the LLaMA-7B attention shape: three 4096 x 4096
+    projections of one token, as one sherry_linear call on the stacked packed
+    weights versus three calls (rotating copies, as for the step)."""
+    w = synth.WORKLOADS["2a"]
+    W = synth.workload_weights(w).cuda()
+    p1, a1 = bw.quantize_pack(W)
+    del W
+    G, nb = 3, w.packed_bytes
+    packed, alpha = bw.concat_packed([(p1, a1)] * G, [w.N] * G, w.K)
+    R = copies_for(G * nb, 0)
+    packs = [packed] + [packed.clone() for _ in range(R - 1)]
+    alphas = [alpha] + [alpha.clone() for _ in range(R - 1)]
+    x = synth.workload_activations(w).cuda()
+    y = torch.empty((1, G * w.N), dtype=torch.float32, device="cuda")
+    ys = [torch.empty((1, w.N), dtype=torch.float32, device="cuda") for _ in range(G)]
+    ws = torch.zeros(max(bw.workspace_bytes(1, G * w.N, w.K), bw.workspace_bytes(1, w.N, w.K), 256),
+                     dtype=torch.uint8, device="cuda")
+    n = max(200, R)
+    one, _ = graph_time(torch, lambda i: bw.linear(x, packs[i % R], alphas[i % R], G * w.N, w.K,
+                                                   out=y, workspace=ws), n, reps=3)
+
+    def three(i):
+        r = i % R
+        for j in range(G):
+            bw.linear(x, packs[r][j * nb:(j + 1) * nb], alphas[r][j * w.N:(j + 1) * w.N], w.N, w.K,
+                      out=ys[j], workspace=ws)
+    sep, _ = graph_time(torch, three, n, reps=3)
+    return {"shape": "3 x (N=4096, K=4096), M=1, fp32 x (sherry_linear)",
+            "one_call_us": round(one * 1e3, 3), "three_calls_us": round(sep * 1e3, 3),
+            "one_call_packed_GB_s": round(G * nb / one / 1e6, 1), "rotating_copies": R}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -373,6 +406,8 @@ def main():
                                        "traffic": traffic_from_profile(
                                            "mfma_gemm", "5", p5["plan"]),
                                        "kernel": "mfma_gemm_kernel"}}
+        out["grouped_qkv"] = grouped_bench(torch, bw, synth)
+        torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
     print(json.dumps(out), flush=True)

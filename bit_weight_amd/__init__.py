@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "SherryError", "lib", "packed_bytes", "workspace_bytes", "plan", "plan_override",
-    "quantize_pack", "quantize_act", "gemm", "gemm_i32", "linear", "linear_scratch_bytes",
+    "quantize_pack", "quantize_act", "gemm", "gemm_i32", "linear", "linear_scratch_bytes", "concat_packed",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -274,3 +274,20 @@ def linear(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, N: int, K
     _check(lib().sherry_linear(px, packed.data_ptr(), alpha.data_ptr(), py, M, N, K, wp, wn, sp, sn,
                                _stream(x.device)), "sherry_linear")
     return out
+
+
+def concat_packed(parts, Ns, K: int):
+    """Group several [N_i, K] packed matrices (e.g. q/k/v or gate/up, all
+    N_i % 64 == 0) into one [sum N_i, K] packed matrix.  The format keeps
+    each 64-row tile of every k-tile contiguous and orders tiles row group
+    first, so stacking weights along N stacks their packed bytes: the group
+    is plain concatenation, and one sherry_linear call on it computes every
+    member's output, sharing one activation quantization and one launch.
+    `parts` are (packed, alpha) pairs; returns (packed, alpha)."""
+    packs, alphas = [], []
+    for (pk, al), n in zip(parts, Ns):
+        if pk.numel() != packed_bytes(n, K) or al.numel() != n:
+            raise RuntimeError("a part has the wrong size for its [N_i, K]")
+        packs.append(pk)
+        alphas.append(al)
+    return torch.cat(packs), torch.cat(alphas)

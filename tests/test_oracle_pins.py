@@ -251,3 +251,13 @@ def test_every_block_has_three_nonzeros_on_workload_data(orc, name):
     assert hist.sum() == T.size
     assert np.all((T.reshape(64, -1, 4) != 0).sum(-1) == 3)
     assert np.all(alpha > 0)
+
+
+def test_packed_layout_stacks_along_n(orc):
+    """Weights stacked along N give stacked packed bytes (row groups are
+    stored one after another), which is what grouping projections relies on."""
+    rng = np.random.default_rng(31)
+    T1 = orc.quantize(rng.normal(0, 0.02, (192, 384)).astype(np.float32))[0]
+    T2 = orc.quantize(rng.normal(0, 0.02, (64, 384)).astype(np.float32))[0]
+    both = orc.pack(np.concatenate([T1, T2]))
+    assert np.array_equal(both, np.concatenate([orc.pack(T1), orc.pack(T2)]))

@@ -319,3 +319,25 @@ def test_linear_workloads(orc, name):
     del W
     _say(f"linear workload {w.description} scratch={bw.linear_scratch_bytes(w.M, w.N, w.K)}")
     _linear_check(orc, x, packed, T, alpha, galpha, w.N, w.K, name)
+
+
+def test_grouped_projections_one_call(orc):
+    """q/k/v-style group: one sherry_linear over the stacked packed weights
+    equals the members' separate calls bit for bit, and the oracle."""
+    K = 1152
+    Ns = [320, 64, 192]
+    Ws = [synth.weights(n, K, 0.02, False, seed=5100 + n) for n in Ns]
+    parts = [gpu_pack(W) for W in Ws]
+    packed, galpha = bw.concat_packed(parts, Ns, K)
+    gstk, astk = gpu_pack(torch.cat(Ws))
+    assert torch.equal(packed, gstk) and torch.equal(galpha, astk)
+    T, alpha = orc.quantize(torch.cat(Ws).numpy())
+    for M in (1, 3, 8):
+        x = synth.activations(M, K, seed=5200 + M)
+        gy = bw.linear(x.cuda(), packed, galpha, sum(Ns), K)
+        sep = torch.cat([bw.linear(x.cuda(), p, a, n, K) for (p, a), n in zip(parts, Ns)], dim=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(gy.cpu().numpy().view(np.uint32), sep.cpu().numpy().view(np.uint32))
+        q, s = orc.act_quant(x.numpy())
+        _, y = orc.gemm(q, s, T, alpha)
+        assert_y_close(gy.cpu().numpy(), y)
