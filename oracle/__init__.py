@@ -51,6 +51,8 @@ def _load():
             "oracle_quantize": [vp, i64, i64, vp, vp],
             "oracle_pack": [vp, i64, i64, vp],
             "oracle_unpack": [vp, i64, i64, vp],
+            "oracle_pack2": [vp, i64, i64, vp],
+            "oracle_unpack2": [vp, i64, i64, vp],
             "oracle_act_quant": [vp, i64, i64, vp, vp],
             "oracle_lut": [vp, i64, i64, vp],
             "oracle_gemm_i32": [vp, vp, i64, i64, i64, vp],
@@ -119,6 +121,24 @@ def unpack(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     assert packed.size == N * K * 5 // 32
     T = np.empty((N, K), np.int8)
     _check(_load().oracle_unpack(_p(packed), N, K, _p(T)), "unpack")
+    return T
+
+
+def pack2(T: np.ndarray) -> np.ndarray:
+    """Dense ternary T -> the 2-bit baseline format (N*K/4 bytes)."""
+    T = np.ascontiguousarray(T, dtype=np.int8)
+    N, K = T.shape
+    out = np.empty(N * K // 4, np.uint8)
+    _check(_load().oracle_pack2(_p(T), N, K, _p(out)), "pack2")
+    return out
+
+
+def unpack2(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """2-bit baseline bytes -> dense T int8 [N,K]."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    assert packed.size == N * K // 4
+    T = np.empty((N, K), np.int8)
+    _check(_load().oracle_unpack2(_p(packed), N, K, _p(T)), "unpack2")
     return T
 
 

@@ -215,6 +215,52 @@ int oracle_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* T) {
   return 0;
 }
 
+// The 2-bit baseline format (the "2-bit ternary packing" the Sherry page
+// compares its 5-bit code against, [Sherry §2.1]): every weight of a
+// ternary T in 2 bits, 0 -> 00, +1 -> 01, -1 -> 11, no sparsity assumed.
+// Tiles of 64 rows x 128 columns, 2048 bytes, in the same row-tile-major
+// order as the 5-bit format.  A row's 128 weights form a 256-bit
+// little-endian string, weight j at bits [2j, 2j+2); bits 0..127 of tile
+// row r sit at tile byte 16*r, bits 128..255 at tile byte 1024 + 16*r.
+int oracle_pack2(const int8_t* T, int64_t N, int64_t K, uint8_t* packed) {
+  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 128 != 0) return -1;
+  std::memset(packed, 0, (size_t)(N * K / 4));
+  const int64_t KT = K / 128;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t k = 0; k < K; ++k) {
+      const int v = T[n * K + k];
+      int code;
+      if (v == 0) code = 0;
+      else if (v == 1) code = 1;
+      else if (v == -1) code = 3;
+      else return -2;
+      const int64_t tile = ((n / 64) * KT + k / 128) * 2048;
+      const int64_t r = n % 64, j = k % 128;
+      const int64_t bit = 2 * j;
+      const int64_t byte = tile + (bit < 128 ? 16 * r + bit / 8 : 1024 + 16 * r + (bit - 128) / 8);
+      packed[byte] |= (uint8_t)(code << (bit % 8));
+    }
+  }
+  return 0;
+}
+
+int oracle_unpack2(const uint8_t* packed, int64_t N, int64_t K, int8_t* T) {
+  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 128 != 0) return -1;
+  const int64_t KT = K / 128;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t tile = ((n / 64) * KT + k / 128) * 2048;
+      const int64_t r = n % 64, j = k % 128;
+      const int64_t bit = 2 * j;
+      const int64_t byte = tile + (bit < 128 ? 16 * r + bit / 8 : 1024 + 16 * r + (bit - 128) / 8);
+      const int code = (packed[byte] >> (bit % 8)) & 3;
+      if (code == 2) return -2;
+      T[n * K + k] = (int8_t)(code == 0 ? 0 : (code == 1 ? 1 : -1));
+    }
+  }
+  return 0;
+}
+
 // Per-token symmetric int8 quantization of activations x [M,K].
 int oracle_act_quant(const float* x, int64_t M, int64_t K, int8_t* q,
                      float* s) {

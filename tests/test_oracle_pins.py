@@ -261,3 +261,36 @@ def test_packed_layout_stacks_along_n(orc):
     T2 = orc.quantize(rng.normal(0, 0.02, (64, 384)).astype(np.float32))[0]
     both = orc.pack(np.concatenate([T1, T2]))
     assert np.array_equal(both, np.concatenate([orc.pack(T1), orc.pack(T2)]))
+
+
+# ------------------------------------------------ 2-bit baseline format
+def test_pack2_golden_layout(orc):
+    """The 2-bit baseline layout against hand-derived bytes."""
+    T = np.zeros((64, 128), np.int8)
+    expect = {}
+    for line in open(os.path.join(GOLDEN, "packed2_layout_64x128.txt")):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        if f[0] == "set":
+            T[int(f[1]), int(f[2])] = int(f[3])
+        elif f[0] == "expect":
+            expect[int(f[1])] = int(f[2], 16)
+    got = orc.pack2(T)
+    want = np.zeros(2048, np.uint8)
+    for b, v in expect.items():
+        want[b] = v
+    assert np.array_equal(got, want)
+
+
+def test_pack2_roundtrip_any_ternary(orc):
+    """Unstructured ternary (any mix of -1/0/+1) survives pack2/unpack2, and
+    the Sherry ternarization does too; a 5-bit and a 2-bit packing of the
+    same T describe the same matrix."""
+    rng = np.random.default_rng(8)
+    T = rng.integers(-1, 2, size=(192, 384)).astype(np.int8)
+    assert np.array_equal(orc.unpack2(orc.pack2(T), 192, 384), T)
+    T3, _ = orc.quantize(rng.normal(0, 0.02, (128, 256)).astype(np.float32))
+    assert np.array_equal(orc.unpack2(orc.pack2(T3), 128, 256),
+                          orc.unpack(orc.pack(T3), 128, 256))
+    assert orc.pack2(T3).size * 5 == orc.pack(T3).size * 8   # 2 vs 1.25 bit per weight
