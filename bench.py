@@ -21,8 +21,10 @@ quantization is fused into the product (as it is for this workload), else
 the product kernel the launch plan picks; "prefill" holds the M=512 decode + int8 MFMA
 product against the 5.0 POP/s int8 peak; "workloads" holds every workload's
 kernel time, and for M <= 16 the time of each small-M path (lookup-table
-GEMV and matrix-core GEMV).  "cpu_baseline" times the CPU oracle (single
-thread) on a bounded sample of the same workload.
+GEMV and matrix-core GEMV); "grouped_qkv" times three projections as one call
+on stacked packed weights against three calls; "two_bit_baseline" times the
+same ternary weights in the plain 2-bit packing.  "cpu_baseline" times the
+CPU oracle (single thread) on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -210,6 +212,35 @@ def cpu_baseline(name: str, seconds: float):
             "sample": f"workload {name} (M={w.M}, K={w.K}, N={w.N}): {n} whole steps "
                       f"(act quant + dense int8 x unpacked-ternary product + epilogue) in "
                       f"{el:.1f} s, {per * 1e3:.2f} ms/step; host {platform.processor() or platform.machine()}"}
+
+
+def two_bit_bench(torch, bw, synth, five_bit_us: dict):
+    """The 2-bit baseline packing of the same ternary weights (the page's own
+    comparison point) on the decode workloads, against the 5-bit product on
+    the same launch plan; both stream their weights from HBM."""
+    res = {}
+    for nm in ("2a", "2c", "3a", "3b", "4"):
+        w = synth.WORKLOADS[nm]
+        W = synth.workload_weights(w).cuda()
+        p2, a2 = bw.quantize_pack2(W)
+        del W
+        nb2 = p2.numel()
+        R = copies_for(nb2, 0)
+        packs = [p2] + [p2.clone() for _ in range(R - 1)]
+        alphas = [a2] + [a2.clone() for _ in range(R - 1)]
+        x = synth.workload_activations(w).cuda()
+        q, s = bw.quantize_act(x)
+        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(max(int(bw.lib().sherry_gemm2_workspace_bytes(w.M, w.N, w.K)), 256),
+                         dtype=torch.uint8, device="cuda")
+        ms, _ = graph_time(torch, lambda i: bw.gemm2(q, s, packs[i % R], alphas[i % R], w.N, w.K,
+                                                     out=y, workspace=ws), max(200, R), reps=3)
+        res[nm] = {"two_bit_us": round(ms * 1e3, 3), "five_bit_us": five_bit_us.get(nm),
+                   "two_bit_bytes": nb2, "five_bit_bytes": w.packed_bytes,
+                   "two_bit_GB_s": round(nb2 / ms / 1e6, 1)}
+        del packs, alphas
+        torch.cuda.empty_cache()
+    return res
 
 
 def grouped_bench(torch, bw, synth):
@@ -407,6 +438,9 @@ def main():
                                            "mfma_gemm", "5", p5["plan"]),
                                        "kernel": "mfma_gemm_kernel"}}
         out["grouped_qkv"] = grouped_bench(torch, bw, synth)
+        torch.cuda.empty_cache()
+        out["two_bit_baseline"] = two_bit_bench(
+            torch, bw, synth, {k: v["path_us"]["decode_mfma_gemv"] for k, v in wl.items() if "path_us" in v})
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)

@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "SherryError", "lib", "packed_bytes", "workspace_bytes", "plan", "plan_override",
-    "quantize_pack", "quantize_act", "gemm", "gemm_i32", "linear", "linear_scratch_bytes", "concat_packed",
+    "quantize_pack", "quantize_act", "gemm", "gemm_i32", "linear", "linear_scratch_bytes", "concat_packed", "quantize_pack2", "gemm2",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
                 "sherry_gemm": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
                 "sherry_gemm_i32": ([vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
                 "sherry_linear_scratch_bytes": ([i64, i64, i64], sz),
+                "sherry_packed2_bytes": ([i64, i64], sz),
+                "sherry_quantize_pack2": ([vp, i64, i64, vp, vp, vp], ci),
+                "sherry_gemm2_workspace_bytes": ([i64, i64, i64], sz),
+                "sherry_gemm2": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
                 "sherry_linear": ([vp, vp, vp, vp, i64, i64, i64, vp, sz, vp, sz, vp], ci),
             }
             for name, (args, res) in sigs.items():
@@ -291,3 +295,45 @@ def concat_packed(parts, Ns, K: int):
         packs.append(pk)
         alphas.append(al)
     return torch.cat(packs), torch.cat(alphas)
+
+
+def quantize_pack2(W: torch.Tensor):
+    """The same ternarization as quantize_pack, in the 2-bit baseline format
+    -> (packed uint8 [N*K/4], alpha fp32 [N])."""
+    pW = _dev_tensor(W, "W", torch.float32)
+    if W.dim() != 2:
+        raise RuntimeError("W must be 2-D [N,K]")
+    N, K = W.shape
+    nb = int(lib().sherry_packed2_bytes(N, K))
+    if nb == 0:
+        raise SherryError(-2, "sherry_quantize_pack2")
+    packed = torch.empty(nb, dtype=torch.uint8, device=W.device)
+    alpha = torch.empty(N, dtype=torch.float32, device=W.device)
+    _check(lib().sherry_quantize_pack2(pW, N, K, packed.data_ptr(), alpha.data_ptr(),
+                                       _stream(W.device)), "sherry_quantize_pack2")
+    return packed, alpha
+
+
+def gemm2(x: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor,
+          N: int, K: int, out: torch.Tensor | None = None,
+          workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The product on the 2-bit baseline format (M <= 16)."""
+    px = _dev_tensor(x, "x", torch.int8)
+    _dev_tensor(packed, "packed", torch.uint8)
+    _dev_tensor(s_x, "s_x", torch.float32)
+    _dev_tensor(alpha, "alpha", torch.float32)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise RuntimeError(f"x must be [M,{K}]")
+    if packed.numel() != int(lib().sherry_packed2_bytes(N, K)):
+        raise RuntimeError("packed has the wrong size for [N,K]")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    py = _dev_tensor(out, "out", torch.float32)
+    ws = workspace if workspace is not None else _workspaces.get(
+        x.device, int(lib().sherry_gemm2_workspace_bytes(M, N, K)))
+    wp = ws.data_ptr() if ws is not None else None
+    wn = ws.numel() if ws is not None else 0
+    _check(lib().sherry_gemm2(px, s_x.data_ptr(), packed.data_ptr(), alpha.data_ptr(), py, M, N, K,
+                              wp, wn, _stream(x.device)), "sherry_gemm2")
+    return out

@@ -65,6 +65,13 @@ __device__ __forceinline__ v4i decode4(uint32_t v, const uint8_t* dec2) {
   return v4i{(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
 }
 
+// B operand of one sub-step in the 2-bit baseline format: 16 weights (one
+// dword of 2-bit codes) as four byte-indexed lookups of 4 int8 weights.
+__device__ __forceinline__ v4i decode16(uint32_t v, const uint32_t* tbl) {
+  return v4i{(int)tbl[v & 255u], (int)tbl[(v >> 8) & 255u], (int)tbl[(v >> 16) & 255u],
+             (int)tbl[v >> 24]};
+}
+
 // 4 x 4 transpose of 16-lane rows: out[t] row g = in[g] row t.
 __device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
                                            uint32_t (&out)[4]) {
@@ -85,10 +92,15 @@ __device__ __forceinline__ float amax4(const float4 v) {
 }
 
 // KW waves share one row tile; MT = the token count rounded up to a power
-// of two (1..16); FQ = fused activation quantization (MT <= 4).
-template <int KW, int MT, bool FQ>
+// of two (1..16); FQ = fused activation quantization (MT <= 4); FMT = code
+// format: 0 = the 5-bit Sherry code, 1 = the 2-bit baseline packing (its
+// tile row is 8 dwords: lane group g takes dwords 2g and 2g+1, the same
+// inputs 32g..32g+31, through the same two transposes).
+template <int KW, int MT, bool FQ, int FMT>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int splits, int kt_per_split) {
   constexpr int NT = 64 * KW;
+  constexpr int TB = FMT == 0 ? kTileBytes : kTile2Bytes;   // bytes per format tile
+  __shared__ __attribute__((aligned(16))) uint32_t tbl2[FMT == 1 ? 256 : 1];
   constexpr int QS = FQ ? kFuseMaxSpan * kTileK : 16;   // int8 activations per token in LDS
   __shared__ __attribute__((aligned(16))) uint2 dec2[1024];
   __shared__ __attribute__((aligned(16))) int red[KW * MT * kRedLd];   // [wave][token][row]
@@ -110,8 +122,8 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   const int nk = span > q ? (span - q + KW - 1) / KW : 0;
 
   // buffer descriptors: this row tile's codes, and the M tokens of x
-  const size_t tb = tile_offset(rt, 0, KT);
-  const __amdgpu_buffer_rsrc_t rc = gemv_rsrc(a.packed + tb, (size_t)KT * kTileBytes);
+  const size_t tb = (size_t)rt * KT * TB;
+  const __amdgpu_buffer_rsrc_t rc = gemv_rsrc(a.packed + tb, (size_t)KT * TB);
   const __amdgpu_buffer_rsrc_t rx = gemv_rsrc(a.x, (size_t)M * (size_t)K);
   // lane offset of the activations (>= M*K for the padding tokens; the
   // k-tile offset is added to it, not passed as the scalar offset, so the
@@ -121,11 +133,15 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
 
   // i-th k-tile of this wave (clamped: the prefetch past the end re-reads
   // the last tile, whose values are never used)
-  auto load = [&](int i, v4u& w, uint32_t& h, v4u& x0, v4u& x1) {
+  auto load = [&](int i, v4u& w, v4u& h, v4u& x0, v4u& x1) {
     const int kt = kt_begin + q + KW * min(i, nk - 1);
-    const int ks = kt * kTileBytes, ka = kt * kTileK;
+    const int ks = kt * TB, ka = kt * kTileK;
     w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
-    h = __builtin_amdgcn_raw_buffer_load_b32(rc, kTileHiOff + 4 * lane, ks, 0);
+    if constexpr (FMT == 0) {
+      h = v4u{__builtin_amdgcn_raw_buffer_load_b32(rc, kTileHiOff + 4 * lane, ks, 0), 0u, 0u, 0u};
+    } else {
+      h = __builtin_amdgcn_raw_buffer_load_b128(rc, kTile2HiOff + 16 * lane, ks, 0);
+    }
     if constexpr (!FQ) {
       x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka, 0, 0);
       x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka + 16, 0, 0);
@@ -143,7 +159,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   // The scheduling barriers keep every refill inside its own step, so a step
   // waits only for its own stage while the newer ones stay in flight.
   v4u cw[kStages];
-  uint32_t ch[kStages];
+  v4u ch[kStages];
   v4u xa[kStages], xb[kStages];
   if (nk > 0) {
 #pragma unroll
@@ -152,7 +168,11 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  for (int i = tid; i < 1024; i += 64 * KW) dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
+  if constexpr (FMT == 0) {
+    for (int i = tid; i < 1024; i += 64 * KW) dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
+  } else {
+    for (int i = tid; i < 256; i += 64 * KW) tbl2[i] = code2_word(i);
+  }
   if constexpr (FQ) {
     // per-token scale over the whole row (every workgroup reads its tokens'
     // rows; four loads in flight per thread per round)
@@ -199,17 +219,23 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   lds_barrier();
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
 
-  auto step = [&](int i, v4u& w, uint32_t& h, v4u& x0, v4u& x1) {
-    // lane (l16, g) of block t <- dwords g (lo) and g+1 (hi) of row 16t+l16
+  auto step = [&](int i, v4u& w, v4u& h, v4u& x0, v4u& x1) {
     uint32_t lo[kBlk], hi[kBlk];
-    transpose4(w.x, w.y, w.z, w.w, lo);
-    transpose4(w.y, w.z, w.w, h, hi);
     uint32_t f0[kBlk], f1[kBlk];
+    if constexpr (FMT == 0) {
+      // lane (l16, g) of block t <- dwords g (lo) and g+1 (hi) of row 16t+l16
+      transpose4(w.x, w.y, w.z, w.w, lo);
+      transpose4(w.y, w.z, w.w, h.x, hi);
 #pragma unroll
-    for (int t = 0; t < kBlk; ++t) {
-      const uint32_t v = __builtin_amdgcn_alignbit(hi[t], lo[t], sh);
-      f0[t] = v;
-      f1[t] = __builtin_amdgcn_alignbit(hi[t] >> sh, v, 20);
+      for (int t = 0; t < kBlk; ++t) {
+        const uint32_t v = __builtin_amdgcn_alignbit(hi[t], lo[t], sh);
+        f0[t] = v;
+        f1[t] = __builtin_amdgcn_alignbit(hi[t] >> sh, v, 20);
+      }
+    } else {
+      // lane (l16, g) of block t <- dwords 2g (sub-step 0) and 2g+1 (sub-step 1)
+      transpose4(w.x, w.z, h.x, h.z, f0);
+      transpose4(w.y, w.w, h.y, h.w, f1);
     }
     v4i a0, a1;
     if constexpr (FQ) {
@@ -227,11 +253,15 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
     load(i + kStages, w, h, x0, x1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < kBlk; ++t)
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, decode4(f0[t], d2), acc[t], 0, 0, 0);
+    for (int t = 0; t < kBlk; ++t) {
+      const v4i b = FMT == 0 ? decode4(f0[t], d2) : decode16(f0[t], tbl2);
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b, acc[t], 0, 0, 0);
+    }
 #pragma unroll
-    for (int t = 0; t < kBlk; ++t)
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, decode4(f1[t], d2), acc[t], 0, 0, 0);
+    for (int t = 0; t < kBlk; ++t) {
+      const v4i b = FMT == 0 ? decode4(f1[t], d2) : decode16(f1[t], tbl2);
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc[t], 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   int i = 0;
@@ -305,27 +335,27 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   }
 }
 
-template <int KW, bool FQ>
+template <int KW, bool FQ, int FMT>
 hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(p.grid), block(64 * KW);
-  if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1, FQ>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2, FQ>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4, FQ>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1, FQ, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2, FQ, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4, FQ, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
   else if constexpr (!FQ) {
-    if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8, false>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, false>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8, false, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, false, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool FQ>
+template <bool FQ, int FMT>
 hipError_t launch_fq(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   switch (p.rw) {
-    case 4: return launch_kw<4, FQ>(p, a, stream);
-    case 8: return launch_kw<8, FQ>(p, a, stream);
-    case 16: return launch_kw<16, FQ>(p, a, stream);
+    case 4: return launch_kw<4, FQ, FMT>(p, a, stream);
+    case 8: return launch_kw<8, FQ, FMT>(p, a, stream);
+    case 16: return launch_kw<16, FQ, FMT>(p, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -341,7 +371,12 @@ bool mfma_gemv_fusable(const GemmPlan& p, int M, int K) {
 
 // plan.rw carries the waves per row tile for this path (4, 8 or 16).
 hipError_t launch_mfma_gemv(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  return a.xf ? launch_fq<true>(p, a, stream) : launch_fq<false>(p, a, stream);
+  return a.xf ? launch_fq<true, 0>(p, a, stream) : launch_fq<false, 0>(p, a, stream);
+}
+
+hipError_t launch_mfma_gemv2(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  if (a.xf) return hipErrorInvalidValue;
+  return launch_fq<false, 1>(p, a, stream);
 }
 
 }  // namespace sherry

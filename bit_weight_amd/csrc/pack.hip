@@ -57,6 +57,37 @@ __global__ __launch_bounds__(64) void pack_codes_kernel(const float* __restrict_
   *reinterpret_cast<uint32_t*>(tile + kTileHiOff + 4 * lane) = w[4];
 }
 
+// The same ternarization written in the 2-bit baseline format: one wave per
+// 64 x 128 tile, lane r = tile row r; weights 0..63 of the row as one
+// 16-byte store, weights 64..127 as another (both coalesced).
+__global__ __launch_bounds__(64) void pack2_codes_kernel(const float* __restrict__ W,
+                                                         uint8_t* __restrict__ packed,
+                                                         int N, int K) {
+  const int KT = K / kTileK;
+  const int rt = blockIdx.x / KT, kt = blockIdx.x % KT;
+  const int lane = threadIdx.x;
+  const int n = rt * kTileRows + lane;
+  if (n >= N) return;
+  const float4* src = reinterpret_cast<const float4*>(W + (size_t)n * K + (size_t)kt * kTileK);
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    const float4 v = src[b];
+    // the block's values from its 5-bit code, then 2 bits per weight
+    const uint32_t cw = code_word(encode_block(v.x, v.y, v.z, v.w));
+    uint32_t bits = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t byte = (cw >> (8 * j)) & 0xFFu;
+      bits |= (byte == 0 ? 0u : (byte == 1 ? 1u : 3u)) << (2 * j);
+    }
+    w[b >> 2] |= bits << (8 * (b & 3));
+  }
+  uint8_t* tile = packed + ((size_t)rt * KT + kt) * kTile2Bytes;
+  *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(tile + kTile2HiOff + 16 * lane) = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
 // One thread per row: alpha[n] = sum of kept |w| in ascending k, in double,
 // divided once by the kept count and rounded once to float.
 __global__ __launch_bounds__(256) void pack_alpha_kernel(const float* __restrict__ W,
@@ -151,6 +182,17 @@ hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, f
                                 hipStream_t stream) {
   const int tiles = (N / kTileRows) * (K / kTileK);
   hipLaunchKernelGGL(pack_codes_kernel, dim3(tiles), dim3(64), 0, stream, W, packed, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_alpha_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, W, alpha,
+                     N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_pack2(const float* W, int N, int K, uint8_t* packed, float* alpha,
+                                 hipStream_t stream) {
+  const int tiles = (N / kTileRows) * (K / kTileK);
+  hipLaunchKernelGGL(pack2_codes_kernel, dim3(tiles), dim3(64), 0, stream, W, packed, N, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pack_alpha_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, W, alpha,

@@ -284,6 +284,57 @@ sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,
                   stream);
 }
 
+size_t sherry_packed2_bytes(int64_t N, int64_t K) {
+  if (!shape_ok(1, N, K)) return 0;
+  return (size_t)N * (size_t)K / 4;
+}
+
+sherry_status sherry_quantize_pack2(const float* W, int64_t N, int64_t K, void* packed, float* alpha,
+                                    void* stream) {
+  if (!W || !packed || !alpha) return SHERRY_ERR_NULL;
+  if (!shape_ok(1, N, K)) return SHERRY_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(alpha, 4)) return SHERRY_ERR_ALIGN;
+  const sherry_status d = check_device();
+  if (d != SHERRY_OK) return d;
+  const hipError_t e = launch_quantize_pack2(W, (int)N, (int)K, static_cast<uint8_t*>(packed), alpha,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+}
+
+size_t sherry_gemm2_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!shape_ok(M, N, K) || M > kLutMaxM) return 0;
+  return plan_mfma_gemv((int)M, (int)N, (int)K).ws_bytes;
+}
+
+sherry_status sherry_gemm2(const int8_t* x, const float* s_x, const void* packed, const float* alpha,
+                           float* y, int64_t M, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!x || !s_x || !packed || !alpha || !y) return SHERRY_ERR_NULL;
+  if (!shape_ok(M, N, K) || M > kLutMaxM) return SHERRY_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 4) || !aligned(s_x, 4) ||
+      !aligned(alpha, 4))
+    return SHERRY_ERR_ALIGN;
+  const GemmPlan plan = plan_mfma_gemv((int)M, (int)N, (int)K);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return SHERRY_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SHERRY_ERR_ALIGN;
+  }
+  const sherry_status d = check_device();
+  if (d != SHERRY_OK) return d;
+  GemmArgs args{};
+  args.x = x;
+  args.s_x = s_x;
+  args.packed = static_cast<const uint8_t*>(packed);
+  args.alpha = alpha;
+  args.y = y;
+  args.M = (int)M;
+  args.N = (int)N;
+  args.K = (int)K;
+  if (plan.ws_bytes > 0) args.partials = static_cast<int32_t*>(workspace);
+  const hipError_t e = launch_mfma_gemv2(plan, args, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+}
+
 size_t sherry_linear_scratch_bytes(int64_t M, int64_t N, int64_t K) {
   if (!shape_ok(M, N, K)) return 0;
   return linear_scratch((int)M, (int)N, (int)K, nullptr, nullptr);

@@ -50,6 +50,24 @@ __host__ __device__ constexpr bool code_word_matches_definition() {
 }
 static_assert(code_word_matches_definition(), "code_word disagrees with code_value");
 
+// 2-bit baseline format (the plain ternary packing the Sherry page compares
+// its 5-bit code against, §2.1): 0 -> 00, +1 -> 01, -1 -> 11; tiles of 64
+// rows x 128 columns, 2048 bytes, row-tile-major; weights 0..63 of tile
+// row r (bits 0..127) at tile byte 16*r, weights 64..127 at 1024 + 16*r.
+constexpr int kTile2Bytes = 2048;
+constexpr int kTile2HiOff = 1024;
+
+// Four 2-bit weights (one byte b) as 4 int8 lanes of a dword.
+__host__ __device__ constexpr uint32_t code2_word(uint32_t b) {
+  uint32_t w = 0;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t c = (b >> (2 * i)) & 3u;
+    const uint32_t v = c == 0 ? 0u : (c == 1 ? 0x01u : 0xFFu);   // 10 is never written
+    w |= v << (8 * i);
+  }
+  return w;
+}
+
 // 5-bit code j (0..31) of a row's 160-bit string held in w[0..4].  Called
 // with a compile-time j inside unrolled loops, so the branch folds away.
 __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[5], int j) {

@@ -49,11 +49,15 @@ struct GemmArgs {
 
 hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, float* alpha,
                                 hipStream_t stream);
+hipError_t launch_quantize_pack2(const float* W, int N, int K, uint8_t* packed, float* alpha,
+                                 hipStream_t stream);
 hipError_t launch_quantize_act(const float* x, int M, int K, int8_t* q, float* s_x,
                                hipStream_t stream);
 hipError_t launch_lut_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 hipError_t launch_mfma_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 bool mfma_gemv_fusable(const GemmPlan& plan, int M, int K);
+// The same GEMV on the 2-bit baseline format (packed = kTile2Bytes tiles).
+hipError_t launch_mfma_gemv2(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 int mfma_gemm_grid(int M, int N);
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 

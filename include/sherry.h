@@ -144,6 +144,37 @@ sherry_status sherry_linear(const float* x, const void* packed, const float* alp
                             void* workspace, size_t workspace_bytes,
                             void* scratch, size_t scratch_bytes, void* stream);
 
+/* --- 2-bit baseline -------------------------------------------------------
+ * The plain ternary packing the Sherry page measures its 5-bit code against
+ * (§2.1: the 5-bit code cuts bit-operation overhead relative to 2-bit
+ * packing): the SAME ternary weights and alpha as sherry_quantize_pack,
+ * written 2 bits per weight (0 -> 00, +1 -> 01, -1 -> 11), so every product
+ * is identical to sherry_gemm's and only the format (2 vs 1.25 bit/weight)
+ * and its decode differ.  Layout: tiles of 64 rows x 128 columns (2048
+ * bytes), row-tile-major; weight j of tile row r at bits [2j, 2j+2) of the
+ * row's 256-bit little-endian string, bits 0..127 at tile byte 16*r and bits
+ * 128..255 at tile byte 1024 + 16*r.  Same shape rules as the 5-bit format. */
+
+/* N*K/4; host-only, pure; 0 for an unsupported shape. */
+size_t sherry_packed2_bytes(int64_t N, int64_t K);
+
+/* As sherry_quantize_pack, output in the 2-bit format (packed: 16-byte
+ * aligned, sherry_packed2_bytes(N,K) bytes). */
+sherry_status sherry_quantize_pack2(const float* W, int64_t N, int64_t K,
+                                    void* packed, float* alpha, void* stream);
+
+/* Scratch bytes of sherry_gemm2 (same zero-fill rule as
+ * sherry_workspace_bytes); 0 when M > 16 or the shape is unsupported. */
+size_t sherry_gemm2_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* The product on the 2-bit format, decode shapes only (1 <= M <= 16, else
+ * SHERRY_ERR_SHAPE): the matrix-core GEMV with the codes decoded through a
+ * 256-entry table (one lookup per 4 weights).  Arguments as sherry_gemm. */
+sherry_status sherry_gemm2(const int8_t* x, const float* s_x, const void* packed,
+                           const float* alpha, float* y, int64_t M, int64_t N,
+                           int64_t K, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Launch plan sherry_gemm uses for a shape (host-only, pure; for
  * diagnostics and benchmarks).  Any output pointer may be NULL.
  *   path: 0 = lookup-table GEMV (per-segment tables in LDS, §2.2),

@@ -173,3 +173,25 @@ def test_linear_scratch_and_validation():
     assert L.sherry_linear(*args(M=M, N=N, K=K, sc=None)) == WS
     assert L.sherry_linear(*args(M=M, N=N, K=K, scb=need_sc - 1)) == WS
     assert L.sherry_linear(*args(M=M, N=N, K=K, sc=FAKE + 64)) == ALIGN
+
+
+def test_two_bit_baseline_sizes_and_validation():
+    L = bw.lib()
+    assert L.sherry_packed2_bytes(4096, 4096) == 4096 * 4096 // 4
+    assert L.sherry_packed2_bytes(64, 100) == 0
+    assert L.sherry_gemm2_workspace_bytes(17, 4096, 4096) == 0          # decode shapes only
+    assert L.sherry_quantize_pack2(None, 64, 128, FAKE, FAKE, None) == NULL
+    assert L.sherry_quantize_pack2(FAKE, 64, 100, FAKE, FAKE, None) == SHAPE
+    assert L.sherry_quantize_pack2(FAKE, 64, 128, FAKE + 4, FAKE, None) == ALIGN
+    g2 = lambda **kw: L.sherry_gemm2(*[kw.get(k, v) for k, v in dict(
+        x=FAKE, s=FAKE, p=FAKE, al=FAKE, y=FAKE, M=1, N=64, K=128, ws=FAKE, wsb=1 << 30,
+        st=None).items()])
+    for k in ("x", "s", "p", "al", "y"):
+        assert g2(**{k: None}) == NULL, k
+    assert g2(M=17) == SHAPE
+    assert g2(K=100) == SHAPE
+    assert g2(p=FAKE + 8) == ALIGN
+    need = L.sherry_gemm2_workspace_bytes(1, 4096, 4096)
+    assert need > 0
+    assert g2(N=4096, K=4096, ws=None) == WS
+    assert g2(N=4096, K=4096, wsb=need - 1) == WS

@@ -341,3 +341,56 @@ def test_grouped_projections_one_call(orc):
         q, s = orc.act_quant(x.numpy())
         _, y = orc.gemm(q, s, T, alpha)
         assert_y_close(gy.cpu().numpy(), y)
+
+
+# --------------------------------------------------- 2-bit baseline format
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_pack2_parity(orc, N, K):
+    """The 2-bit packer writes the oracle's 2-bit encoding of the same T, and
+    the same alpha as the 5-bit packer."""
+    W = synth.weights(N, K, 0.1, True, seed=6100 + N)
+    T, alpha = orc.quantize(W.numpy())
+    p2, a2 = bw.quantize_pack2(W.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(p2.cpu().numpy(), orc.pack2(T))
+    assert np.array_equal(a2.cpu().numpy().view(np.uint32), alpha.view(np.uint32))
+
+
+@pytest.mark.parametrize("rw,splits", [(4, 0), (4, 3), (8, 1), (16, 2)])
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+@pytest.mark.parametrize("N,K", [(320, 1152), (64, 128)])
+def test_gemm2_parity(orc, rw, splits, M, N, K):
+    """The 2-bit product equals the oracle and is bit-identical to the 5-bit
+    product of the same weights."""
+    W = synth.weights(N, K, 0.02, False, seed=6200 + N + K)
+    T, alpha = orc.quantize(W.numpy())
+    p5, a5 = gpu_pack(W)
+    p2, a2 = bw.quantize_pack2(W.cuda())
+    q = synth.int8_uniform(M, K, seed=6300 + M)
+    s_x = (torch.rand(M, generator=torch.Generator().manual_seed(M + 3)) * 0.05 + 0.001).float()
+    acc, y = orc.gemm(q.numpy(), s_x.numpy(), T, alpha)
+    try:
+        bw.plan_override("decode_mfma_gemv", rw, 0, splits)
+        gy2 = bw.gemm2(q.cuda(), s_x.cuda(), p2, a2, N, K)
+        gy5 = bw.gemm(q.cuda(), s_x.cuda(), p5, a5, N, K)
+        torch.cuda.synchronize()
+    finally:
+        bw.plan_override()
+    assert np.array_equal(gy2.cpu().numpy().view(np.uint32), gy5.cpu().numpy().view(np.uint32))
+    assert_y_close(gy2.cpu().numpy(), y)
+
+
+@pytest.mark.parametrize("name", ["2a", "3b", "4"])
+def test_gemm2_workloads(orc, name):
+    w = synth.WORKLOADS[name]
+    W = synth.workload_weights(w)
+    x = synth.workload_activations(w)
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    _, y = orc.gemm(q, s, T, alpha)
+    p2, a2 = bw.quantize_pack2(W.cuda())
+    del W
+    gy = bw.gemm2(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), p2, a2, w.N, w.K)
+    torch.cuda.synchronize()
+    assert np.array_equal(p2.cpu().numpy(), orc.pack2(T))
+    assert_y_close(gy.cpu().numpy(), y)
