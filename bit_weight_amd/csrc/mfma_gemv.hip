@@ -1,7 +1,8 @@
-// Small-M (decode, M <= 16) product on the matrix cores: the 5-bit codes
-// are decoded to int8 {-1,0,+1} in registers and contracted with the int8
-// activations by v_mfma_i32_16x16x64_i8, the M tokens padded to the
-// instruction's 16 rows.  y = ((float)acc * s_x[m]) * alpha[n] as in every
+// Small-M (decode and short chunks, M <= 64) product on the matrix cores:
+// the 5-bit codes are decoded to int8 {-1,0,+1} in registers and contracted
+// with the int8 activations by v_mfma_i32_16x16x64_i8, the M tokens padded
+// to whole blocks of the instruction's 16 rows (one decoded operand feeds
+// the instruction of every block).  y = ((float)acc * s_x[m]) * alpha[n] as in every
 // path.  [Sherry page §2.2] computes the same integer sums through
 // per-segment tables of pattern dot products; on gfx950 a decoded code pair
 // feeds 8 multiply-adds per token of a matrix-core instruction for one LDS
@@ -25,7 +26,7 @@
 //    16t..16t+15 to lane group g of block t with two 4 x 4 transposes of
 //    16-lane rows (v_permlane32_swap, then v_permlane16_swap).  A 1024-entry
 //    LDS table maps a 10-bit code pair to its 8 int8 weights.
-//  * A operand: lane (l % 16, g) holds token l % 16, inputs 32g + 16s .. +15
+//  * A operand: lane (l % 16, g) holds token 16b + l % 16 of block b, inputs 32g + 16s .. +15
 //    of the k-tile in sub-step s (the same input order as B, which the dot
 //    product does not see).  Loaded straight from global memory through a
 //    buffer descriptor whose range ends at token M, so the padding tokens
@@ -50,7 +51,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kBlk = kTileRows / 16;   // MFMA column blocks per wave
-constexpr int kStages = 4;             // k-tiles of codes and activations in flight per wave
 constexpr int kRedLd = kTileRows + 4;  // words per token row of the epilogue tile
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, size_t bytes) {
@@ -91,13 +91,17 @@ __device__ __forceinline__ float amax4(const float4 v) {
   return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
-// KW waves share one row tile; MT = the token count rounded up to a power
-// of two (1..16); FQ = fused activation quantization (MT <= 4); FMT = code
-// format: 0 = the 5-bit Sherry code, 1 = the 2-bit baseline packing (its
-// tile row is 8 dwords: lane group g takes dwords 2g and 2g+1, the same
-// inputs 32g..32g+31, through the same two transposes).
-template <int KW, int MT, bool FQ, int FMT>
+// KW waves share one row tile; MT = the token count of one MFMA token block
+// rounded up to a power of two (1..16); MB = token blocks of 16 (MB > 1 only
+// with MT = 16: up to 64 tokens, each decoded code feeding MB instructions);
+// FQ = fused activation quantization (MT <= 4); FMT = code format: 0 = the
+// 5-bit Sherry code, 1 = the 2-bit baseline packing (its tile row is 8
+// dwords: lane group g takes dwords 2g and 2g+1, the same inputs
+// 32g..32g+31, through the same two transposes).  ST = register stages.
+template <int KW, int MT, int MB, bool FQ, int FMT, int ST>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int splits, int kt_per_split) {
+  static_assert(MB == 1 || (MT == 16 && !FQ), "several token blocks are whole blocks of 16");
+  constexpr int kStages = ST;
   constexpr int NT = 64 * KW;
   constexpr int TB = FMT == 0 ? kTileBytes : kTile2Bytes;   // bytes per format tile
   __shared__ __attribute__((aligned(16))) uint32_t tbl2[FMT == 1 ? 256 : 1];
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
 
   // i-th k-tile of this wave (clamped: the prefetch past the end re-reads
   // the last tile, whose values are never used)
-  auto load = [&](int i, v4u& w, v4u& h, v4u& x0, v4u& x1) {
+  auto load = [&](int i, v4u& w, v4u& h, v4u (&x0)[MB], v4u (&x1)[MB]) {
     const int kt = kt_begin + q + KW * min(i, nk - 1);
     const int ks = kt * TB, ka = kt * kTileK;
     w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
@@ -142,25 +146,30 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
     } else {
       h = __builtin_amdgcn_raw_buffer_load_b128(rc, kTile2HiOff + 16 * lane, ks, 0);
     }
-    if constexpr (!FQ) {
-      x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka, 0, 0);
-      x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + ka + 16, 0, 0);
-    } else {
-      x0 = v4u{0u, 0u, 0u, 0u};
-      x1 = v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      if constexpr (!FQ) {
+        x0[b] = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + 16 * b * K + ka, 0, 0);
+        x1[b] = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + 16 * b * K + ka + 16, 0, 0);
+      } else {
+        x0[b] = v4u{0u, 0u, 0u, 0u};
+        x1[b] = v4u{0u, 0u, 0u, 0u};
+      }
     }
   };
 
-  v4i acc[kBlk];
+  v4i acc[MB][kBlk];
 #pragma unroll
-  for (int t = 0; t < kBlk; ++t) acc[t] = v4i{0, 0, 0, 0};
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t) acc[b][t] = v4i{0, 0, 0, 0};
 
   // kStages register stages, filled kStages k-tiles ahead and used in turn.
   // The scheduling barriers keep every refill inside its own step, so a step
   // waits only for its own stage while the newer ones stay in flight.
   v4u cw[kStages];
   v4u ch[kStages];
-  v4u xa[kStages], xb[kStages];
+  v4u xa[kStages][MB], xb[kStages][MB];
   if (nk > 0) {
 #pragma unroll
     for (int st = 0; st < kStages; ++st) {
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   lds_barrier();
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
 
-  auto step = [&](int i, v4u& w, v4u& h, v4u& x0, v4u& x1) {
+  auto step = [&](int i, v4u& w, v4u& h, v4u (&x0)[MB], v4u (&x1)[MB]) {
     uint32_t lo[kBlk], hi[kBlk];
     uint32_t f0[kBlk], f1[kBlk];
     if constexpr (FMT == 0) {
@@ -237,30 +246,35 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
       transpose4(w.x, w.z, h.x, h.z, f0);
       transpose4(w.y, w.w, h.y, h.w, f1);
     }
-    v4i a0, a1;
+    v4i a0[MB], a1[MB];
     if constexpr (FQ) {
       // token l16 (zero past M), inputs 32g + 16s of this wave's i-th k-tile
       const uint32_t* src = &qs[(min(l16, M - 1) * QS + (q + KW * i) * kTileK + 32 * g) / 4];
       const v4i v0 = __builtin_bit_cast(v4i, *reinterpret_cast<const v4u*>(src));
       const v4i v1 = __builtin_bit_cast(v4i, *reinterpret_cast<const v4u*>(src + 4));
       const v4i z{0, 0, 0, 0};
-      a0 = l16 < M ? v0 : z;
-      a1 = l16 < M ? v1 : z;
+      a0[0] = l16 < M ? v0 : z;
+      a1[0] = l16 < M ? v1 : z;
     } else {
-      a0 = __builtin_bit_cast(v4i, x0);
-      a1 = __builtin_bit_cast(v4i, x1);
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        a0[b] = __builtin_bit_cast(v4i, x0[b]);
+        a1[b] = __builtin_bit_cast(v4i, x1[b]);
+      }
     }
     load(i + kStages, w, h, x0, x1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
-      const v4i b = FMT == 0 ? decode4(f0[t], d2) : decode16(f0[t], tbl2);
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b, acc[t], 0, 0, 0);
+      const v4i bw = FMT == 0 ? decode4(f0[t], d2) : decode16(f0[t], tbl2);
+#pragma unroll
+      for (int b = 0; b < MB; ++b) acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[b], bw, acc[b][t], 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
-      const v4i b = FMT == 0 ? decode4(f1[t], d2) : decode16(f1[t], tbl2);
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc[t], 0, 0, 0);
+      const v4i bw = FMT == 0 ? decode4(f1[t], d2) : decode16(f1[t], tbl2);
+#pragma unroll
+      for (int b = 0; b < MB; ++b) acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[b], bw, acc[b][t], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -273,64 +287,68 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   for (int st = 0; st < kStages - 1; ++st)
     if (i + st < nk) step(i + st, cw[st], ch[st], xa[st], xb[st]);
 
-  // Epilogue.  Every wave writes its sums to LDS as [token][row]; then each
-  // lane owns one weight row and a fixed set of tokens, so the K-split
-  // atomics of a lane are issued back to back with no branch between them
-  // and cost one memory round trip.  Tokens from M up to the padded count MT
-  // add 0 to the cell of token M-1, which changes nothing.
-#pragma unroll
-  for (int t = 0; t < kBlk; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (4 * g + j < MT) red[(q * MT + 4 * g + j) * kRedLd + 16 * t + l16] = acc[t][j];
-  __syncthreads();
-  constexpr int TPW = MT >= KW ? MT / KW : 1;        // tokens per wave
-  if (q * TPW >= MT) return;
+  // Epilogue, one token block at a time.  Every wave writes its sums to LDS
+  // as [token][row]; then each lane owns one weight row and a fixed set of
+  // tokens, so the K-split atomics of a lane are issued back to back with no
+  // branch between them and cost one memory round trip.  Tokens from M up to
+  // the padded count add 0 to the cell of token M-1, which changes nothing.
+  constexpr int TPW = MT >= KW ? MT / KW : 1;        // tokens per wave and block
   const int n = rt * kTileRows + lane;
   const float al = a.y ? a.alpha[n] : 0.0f;
-  int total[TPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int m = q * TPW + i;
-    int v = 0;
+  for (int b = 0; b < MB; ++b) {
+    if (b > 0) __syncthreads();   // the previous block's sums are read
 #pragma unroll
-    for (int qq = 0; qq < KW; ++qq) v += red[(qq * MT + m) * kRedLd + lane];
-    total[i] = v;
-  }
-  bool last[TPW];
+    for (int t = 0; t < kBlk; ++t)
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) last[i] = true;
-  if (splits > 1) {
-    unsigned long long* cells = reinterpret_cast<unsigned long long*>(a.partials);
-    unsigned long long now[TPW];
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j < MT) red[(q * MT + 4 * g + j) * kRedLd + 16 * t + l16] = acc[b][t][j];
+    __syncthreads();
+    if (q * TPW >= MT) continue;
+    int total[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int m = q * TPW + i;
-      const unsigned long long inc =
-          m < M ? (1ull << 32) + (unsigned long long)(long long)total[i] : 0ull;
-      now[i] = __hip_atomic_fetch_add(cells + (size_t)min(m, M - 1) * N + n, inc, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
+      int v = 0;
+#pragma unroll
+      for (int qq = 0; qq < KW; ++qq) v += red[(qq * MT + m) * kRedLd + lane];
+      total[i] = v;
+    }
+    bool last[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) last[i] = true;
+    if (splits > 1) {
+      unsigned long long* cells = reinterpret_cast<unsigned long long*>(a.partials);
+      unsigned long long now[TPW];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int m = 16 * b + q * TPW + i;
+        const unsigned long long inc =
+            m < M ? (1ull << 32) + (unsigned long long)(long long)total[i] : 0ull;
+        now[i] = __hip_atomic_fetch_add(cells + (size_t)min(m, M - 1) * N + n, inc, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int m = 16 * b + q * TPW + i;
+        now[i] += (1ull << 32) + (unsigned long long)(long long)total[i];
+        total[i] = (int)(uint32_t)now[i];
+        // the high word minus the borrow of a negative low word = arrivals
+        last[i] = (((long long)now[i] - (long long)total[i]) >> 32) == (long long)splits;
+        if (m < M && last[i])
+          __hip_atomic_store(cells + (size_t)m * N + n, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int m = q * TPW + i;
-      now[i] += (1ull << 32) + (unsigned long long)(long long)total[i];
-      total[i] = (int)(uint32_t)now[i];
-      // the high word minus the borrow of a negative low word = arrivals
-      last[i] = (((long long)now[i] - (long long)total[i]) >> 32) == (long long)splits;
-      if (m < M && last[i])
-        __hip_atomic_store(cells + (size_t)m * N + n, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int m = q * TPW + i;
-    if (m >= M || !last[i]) continue;
-    if (a.y) {
-      const float tv = (float)total[i] * (FQ ? sred[KW * MT + m] : a.s_x[m]);
-      a.y[(size_t)m * N + n] = tv * al;
-    } else {
-      a.acc[(size_t)m * N + n] = total[i];
+      const int m = 16 * b + q * TPW + i;
+      if (m >= M || !last[i]) continue;
+      if (a.y) {
+        const float tv = (float)total[i] * (FQ ? sred[KW * MT + m] : a.s_x[m]);
+        a.y[(size_t)m * N + n] = tv * al;
+      } else {
+        a.acc[(size_t)m * N + n] = total[i];
+      }
     }
   }
 }
@@ -338,12 +356,19 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
 template <int KW, bool FQ, int FMT>
 hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(p.grid), block(64 * KW);
-  if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1, FQ, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2, FQ, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4, FQ, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1, 1, FQ, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2, 1, FQ, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4, 1, FQ, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
   else if constexpr (!FQ) {
-    if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8, false, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, false, FMT>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 16) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if constexpr (FMT == 0 && KW <= 8) {   // 16 waves leave too few registers for two blocks
+      if (a.M <= 32) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, 2, false, 0, 3>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+      else if (a.M <= kGemvMaxM) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, 4, false, 0, 2>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+      else return hipErrorInvalidValue;
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
     return hipErrorInvalidValue;
   }

@@ -56,7 +56,8 @@ GemmPlan plan_mfma_gemv(int M, int N, int K) {
   GemmPlan p{};
   const int KT = K / kTileK, RT = N / kTileRows;
   const int ovr_kw = g_ovr_rw.load();
-  const int kw = ovr_kw == 4 || ovr_kw == 8 || ovr_kw == 16 ? ovr_kw : (RT >= 128 ? 8 : 4);
+  int kw = ovr_kw == 4 || ovr_kw == 8 || ovr_kw == 16 ? ovr_kw : (RT >= 128 ? 8 : 4);
+  if (M > 16 && kw > 8) kw = 8;   // several token blocks: at most 8 waves
   int splits = 1;
   if (g_ovr_splits.load() > 0) {
     splits = g_ovr_splits.load();
@@ -72,7 +73,7 @@ GemmPlan plan_mfma_gemv(int M, int N, int K) {
   const int kt_per_split = (KT + splits - 1) / splits;
   splits = (KT + kt_per_split - 1) / kt_per_split;
   int mt = 1;
-  while (mt < M) mt *= 2;
+  while (mt < M && mt < 16) mt *= 2;
   p.path = 2;
   p.groups = RT;
   p.rw = kw;            // waves per row tile on this path
@@ -96,6 +97,8 @@ void set_plan_override(int path, int rw, int ch, int splits) {
 
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
+  const int ovr = g_ovr_path.load();
+  if (M > kLutMaxM && M <= kGemvMaxM && ovr != 1) return plan_mfma_gemv(M, N, K);
   if (M > kLutMaxM) {
     p.path = 1;
     p.grid = mfma_gemm_grid(M, N);
@@ -106,7 +109,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
     p.ws_bytes = 0;
     return p;
   }
-  const int path = g_ovr_path.load() >= 0 ? g_ovr_path.load() : kDefaultSmallMPath;
+  const int path = ovr >= 0 ? ovr : kDefaultSmallMPath;
   if (path == 1) {
     GemmPlan q = plan_gemm(kLutMaxM + 1, N, K);
     return q;

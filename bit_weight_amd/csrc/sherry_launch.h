@@ -10,7 +10,7 @@ namespace sherry {
 // Launch plan of the product for one shape (host-side, pure).
 struct GemmPlan {
   int path;          // 0 = lookup-table GEMV, 1 = decode + int8 MFMA GEMM,
-                     // 2 = decode + int8 MFMA GEMV (M <= 16)
+                     // 2 = decode + int8 MFMA GEMV (M <= 64)
   int grid;          // workgroups
   int block;         // threads per workgroup
   int splits;        // K-splits per row group (GEMV)
@@ -23,6 +23,7 @@ struct GemmPlan {
 };
 
 constexpr int kLutMaxM = 16;          // M <= 16 takes a GEMV path
+constexpr int kGemvMaxM = 64;         // 16 < M <= 64: the matrix-core GEMV, unless path 1 is forced
 constexpr int kGemvWaves = 4;         // waves per GEMV workgroup
 constexpr int kDefaultSmallMPath = 2;  // M <= 16: 0 = lookup tables, 2 = matrix-core GEMV
 constexpr int kFuseMaxM = 4;           // fused quantization: at most 4 tokens,

@@ -153,12 +153,13 @@ GEMV_PLANS = [(4, 0), (4, 1), (4, 2), (4, 3), (4, 9), (8, 0), (8, 1), (8, 2), (1
 
 
 @pytest.mark.parametrize("rw,splits", GEMV_PLANS)
-@pytest.mark.parametrize("M", [1, 2, 5, 8, 13, 16])
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 13, 16, 17, 31, 32, 33, 50, 64])
 @pytest.mark.parametrize("N,K", [(320, 1152), (64, 128)])
 def test_gemm_mfma_gemv_plans(orc, packed_cases, rw, splits, M, N, K):
     """Every launch shape of the small-M matrix-core GEMV (waves per row tile
-    incl. idle ones, K-splits incl. ragged ones) gives the same exact result,
-    and the fp32 output matches the oracle."""
+    incl. idle ones, K-splits incl. ragged ones, one to four token blocks of
+    16 with a ragged last block) gives the same exact result, and the fp32
+    output matches the oracle."""
     T, alpha, packed, galpha = packed_cases[(N, K)]
     q = synth.int8_uniform(M, K, seed=1900 + M + K)
     s_x = (torch.rand(M, generator=torch.Generator().manual_seed(M + 7)) * 0.05 + 0.001).float()
@@ -175,9 +176,9 @@ def test_gemm_mfma_gemv_plans(orc, packed_cases, rw, splits, M, N, K):
     assert_y_close(gy.cpu().numpy(), y)
 
 
-@pytest.mark.parametrize("M", [1, 7, 16])
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64])
 def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M):
-    """The M > 16 kernel forced onto a small M (rows past M clamped)."""
+    """The prefill kernel forced onto a small M (rows past M clamped)."""
     N, K = 320, 1152
     T, alpha, packed, galpha = packed_cases[(N, K)]
     q = synth.int8_uniform(M, K, seed=2900 + M)
