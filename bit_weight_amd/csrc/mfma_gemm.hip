@@ -13,9 +13,14 @@
 // A decoded weight operand therefore feeds 8 MFMAs and an activation
 // fragment 4, which keeps the LDS work per k-tile (pair-table lookups plus
 // activation fragments) well below the matrix-core time.
-//  * activations: 128 x 128 int8 per k-step, loaded once per workgroup into a
-//    double-buffered, chunk-major LDS tile (see a_slot), read as MFMA A
-//    operands (16 bytes per lane) without bank conflicts;
+//  * activations: 128 x 128 int8 per k-step, copied once per workgroup
+//    straight from global memory into LDS by buffer loads with LDS return
+//    (no registers on the way), 8 lanes per 128-byte row so every load reads
+//    whole lines; rows sit in a row-major tile whose 16-byte chunks are
+//    XOR-swizzled (see a_off) so the MFMA A reads (16 rows, one chunk) hit 16
+//    different bank groups.  Three buffers per parity: the copy for k-step
+//    j+2 starts right after the barrier of step j, once every wave is done
+//    with the buffer it overwrites, and has two steps to land;
 //  * weights: each wave decodes exactly the B operands it consumes.  It loads
 //    its row tile's 1280-byte k-tile coalesced (lane r = tile row r, 16 + 4
 //    bytes) and moves dwords g and g+1 of rows 16t..16t+15 to lane group g of
@@ -26,10 +31,13 @@
 //    second in sub-step 1); the A operands use the same input order, which a
 //    dot product does not see.  A 1024-entry LDS table maps a 10-bit code
 //    pair to its 8 int8 weights, so 4 codes cost two 8-byte lookups;
-//  * codes and activations come through buffer descriptors (32-bit lane
-//    offsets, scalar k-step offset) two k-steps ahead into two register
-//    stages used in turn; the barrier orders LDS only, so the prefetched
-//    loads stay in flight across it.
+//  * codes come through a buffer descriptor into two register stages used
+//    in turn; a k-step's codes are decoded (table lookups) between the
+//    MFMAs of the step before it, so the LDS lookups overlap matrix-core
+//    work, and the 64 MFMAs of a step run back to back with the A reads two
+//    row blocks ahead.  The barrier waits for exactly the activation copy of
+//    its own step (a counted vmcnt), so the newer loads stay in flight
+//    across it.
 // Tiles are numbered so that the 8 XCDs (workgroups are dealt round-robin)
 // each own a slab of weight rows, which then stays in that XCD's L2 for all
 // activation tiles.
@@ -47,18 +55,27 @@ constexpr int kMT = kBM / 16;                   // 8 row blocks per wave
 constexpr int kNT = kTileRows / 16;             // 4 column blocks per wave (one row tile)
 constexpr int kBK = kTileK;                     // 128
 constexpr int kAStage = kBM * kBK;              // 16 KB per k-step
-constexpr int kAPerThread = kAStage / 16 / 256; // 16-byte chunks each thread stages (4)
+constexpr int kABufs = 3;                       // activation buffers per parity
+constexpr int kACopies = kAStage / 1024 / 4;    // 1 KB copies per wave per k-step (4)
 constexpr int kThreads = 512;                   // 4 row tiles x 2 k-tile parities
-constexpr int kOutLd = kBN + 4;                 // words per row of the epilogue tile (+16 B)
-constexpr int kLdsMain = 4 * kAStage + 8192;    // 2 buffers x 2 parities + pair table
-constexpr int kLdsOut = 16 * kOutLd * 4;        // epilogue tile (16 rows)
+constexpr int kOutLd = kBN + 16;                // words per row of the epilogue tiles (the 4
+                                                // row groups of an MFMA block hit 4 bank quarters)
+constexpr int kLdsMain = 2 * kABufs * kAStage;  // activation buffers x parities
+constexpr int kLdsOut = 2 * 32 * kOutLd * 4;    // epilogue tiles (32 rows, both parities)
 constexpr int kLdsBytes = kLdsMain > kLdsOut ? kLdsMain : kLdsOut;
+// vector-memory ops a wave issues between a k-step's activation copy and
+// that step's barrier: the codes three steps ahead of it (2), the next
+// step's copy, and the codes four steps ahead (2)
+constexpr int kNewerLoads = 2 + kACopies + 2;
 
-// Activation tile in LDS, chunk-major: the 16-byte chunk c of row r sits at
-// slot c * kBM + (r ^ c).  A wave's fragment read (16 consecutive rows, one
-// chunk) covers 256 contiguous bytes, and a row-contiguous write (8 lanes,
-// one row, chunks 0..7) hits 8 different bank groups.
-__device__ __forceinline__ int a_slot(int r, int c) { return (c * kBM + (r ^ c)) * 16; }
+// Activation tile in LDS, row-major with 128-byte rows: the 16-byte chunk c
+// of row r sits at chunk position c ^ ((r >> 1) & 7).  A fragment read (16
+// consecutive rows, one chunk) then spreads over all 16 bank groups of a
+// 256-byte bank period, and 8 lanes copying one row fill one row.
+__device__ __forceinline__ int a_off(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 16; }
+
+// s_waitcnt operand: vmcnt(vm), lgkmcnt(0), expcnt not waited.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 0x70; }
 
 // 4 x 4 transpose of 16-lane rows: out[t] row g = in[g] row t.
 __device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
@@ -75,44 +92,58 @@ __device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2
   out[3] = t23[1];
 }
 
-// Decode of one MFMA sub-step: 4 codes per row into B operands (two 10-bit
-// code pairs, one 8-byte table entry each).
-__device__ __forceinline__ void mg_decode(v4i (&bop)[kNT], const uint32_t (&f)[kNT],
-                                          const uint8_t* dec2) {
-#pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    const uint32_t v = f[t];
-    const uint2 e0 = *reinterpret_cast<const uint2*>(dec2 + ((v << 3) & 0x1FF8u));
-    const uint2 e1 = *reinterpret_cast<const uint2*>(dec2 + ((v >> 7) & 0x1FF8u));
-    bop[t] = v4i{(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
-  }
+// B operands of one column block and sub-step: 4 codes (20 bits of v) as
+// two code pairs, one 8-byte table entry each.
+__device__ __forceinline__ v4i mg_decode4(uint32_t v, const uint8_t* dec2) {
+  const uint2 e0 = *reinterpret_cast<const uint2*>(dec2 + ((v << 3) & 0x1FF8u));
+  const uint2 e1 = *reinterpret_cast<const uint2*>(dec2 + ((v >> 7) & 0x1FF8u));
+  return v4i{(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
 }
 
-// The 8 x 4 MFMAs of one sub-step (A chunk c of the k-step tile at `as`).
-// The A fragments of the next two row blocks are requested before the
-// MFMAs of the current two, so the LDS latency hides behind 8 MFMAs.
-__device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&bop)[kNT],
-                                        const int8_t* as, int l16, int c) {
-  auto frag = [&](int i) { return *reinterpret_cast<const v4i*>(as + a_slot(16 * i + l16, c)); };
-  v4i a0 = frag(0), a1 = frag(1);
+// The 2 x 8 x 4 MFMAs of one k-step (sub-steps s = 0, 1 read A chunk 2g+s
+// of the tile at `as`, with B operands b0 / b1), and the table lookups that
+// decode the next k-step's codes (f0 / f1) into n0 / n1: those of sub-step
+// 0 spread over the last four groups of 8 MFMAs (b0 is dead by then, so n0
+// can take its registers), those of sub-step 1 after the MFMAs.  The A
+// fragments of the next two row blocks are requested before the MFMAs of
+// the current two, so the LDS latency hides behind 8 MFMAs.
+template <bool kLive>
+__device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kNT],
+                                        const v4i (&b1)[kNT], const int8_t* as, int l16, int g,
+                                        const uint32_t (&f0)[kNT], const uint32_t (&f1)[kNT],
+                                        v4i (&n0)[kNT], v4i (&n1)[kNT], const uint8_t* dec2) {
+  auto frag = [&](int u) {   // u = 8 s + row block
+    return *reinterpret_cast<const v4i*>(as + a_off(16 * (u & 7) + l16, 2 * g + (u >> 3)));
+  };
+  v4i a0{0, 0, 0, 0}, a1{0, 0, 0, 0};
+  if constexpr (kLive) {
+    a0 = frag(0);
+    a1 = frag(1);
+  }
 #pragma unroll
-  for (int i = 0; i < kMT; i += 2) {
-    v4i n0 = a0, n1 = a1;
-    if (i + 2 < kMT) {
-      n0 = frag(i + 2);
-      n1 = frag(i + 3);
+  for (int u = 0; u < 2 * kMT; u += 2) {
+    v4i p0 = a0, p1 = a1;
+    if (kLive && u + 2 < 2 * kMT) {
+      p0 = frag(u + 2);
+      p1 = frag(u + 3);
+    }
+    if (u >= kMT) n0[(u >> 1) & 3] = mg_decode4(f0[(u >> 1) & 3], dec2);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kLive) {
+      const int i = u & 7;
+#pragma unroll
+      for (int c = 0; c < kNT; ++c)
+        acc[i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, u < kMT ? b0[c] : b1[c], acc[i][c], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < kNT; ++c)
+        acc[i + 1][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, u < kMT ? b0[c] : b1[c], acc[i + 1][c], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < kNT; ++t)
-      acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bop[t], acc[i][t], 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < kNT; ++t)
-      acc[i + 1][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bop[t], acc[i + 1][t], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    a0 = n0;
-    a1 = n1;
+    a0 = p0;
+    a1 = p1;
   }
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) n1[t] = mg_decode4(f1[t], dec2);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, size_t bytes) {
@@ -121,12 +152,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_tiles) {
-  // one LDS block: the activation buffers [buffer][parity], then the pair
-  // table; after the main loop the epilogue tile reuses all of it
+  // the activation buffers [buffer][parity]; after the main loop the
+  // epilogue tile reuses them
   // (32-bit words: every view below is a character type or 32-bit lanes)
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsBytes / 4];
-  int8_t (*As)[kAStage] = reinterpret_cast<int8_t (*)[kAStage]>(lds);
-  uint2* dec2 = reinterpret_cast<uint2*>(lds + 4 * kAStage / 4);
+  // the pair table in an array of its own: the compiler then sees that its
+  // lookups cannot read what an activation copy in flight is writing
+  __shared__ __attribute__((aligned(16))) uint2 dec2[1024];
+  __shared__ float sxs[kBM];   // s_x of this tile's rows (epilogue)
 
   const int M = a.M, N = a.N, K = a.K, KT = K / kTileK, RT = N / kTileRows;
   // tile id -> (m tile, n tile): consecutive ids of one XCD share n tiles
@@ -159,16 +192,18 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
       buffer_rsrc(a.x + (size_t)m0 * K, (size_t)(M - m0) * (size_t)K);
   const uint32_t sh = 8u * (uint32_t)g;  // bit 40g mod 32
 
-  // activations: each parity's 256 threads stage its k-tile, 128 rows x 128
-  // bytes, four 16-byte chunks per thread (8 lanes per row: coalesced); rows
-  // past M read row M-1 (they feed only unstored output rows)
-  int a_v[kAPerThread], a_lds[kAPerThread];
+  // activations: the 4 waves of a parity copy its k-tile, 128 rows x 128
+  // bytes; copy jj of wave `wave` fills rows 32 wave + 8 jj .. +7, lane L
+  // taking chunk (L & 7) ^ swizzle of row L >> 3 (its LDS position is fixed
+  // at 16 L).  Rows past M read row M-1 (they feed only unstored rows).
+  int a_v[kACopies];
 #pragma unroll
-  for (int i = 0; i < kAPerThread; ++i) {
-    const int idx = (tid & 255) + 256 * i, row = idx >> 3, c = idx & 7;
-    a_v[i] = min(row, M - 1 - m0) * K + c * 16;
-    a_lds[i] = a_slot(row, c);
+  for (int jj = 0; jj < kACopies; ++jj) {
+    const int row = 32 * wave + 8 * jj + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    a_v[jj] = min(row, M - 1 - m0) * K + c * 16;
   }
+  auto a_buf = [&](int b) { return reinterpret_cast<int8_t*>(lds) + (b * 2 + kh) * kAStage; };
 
   v4i acc[kMT][kNT];
 #pragma unroll
@@ -176,137 +211,160 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-  // Codes (coalesced, lane = tile row) and activations of this wave's
-  // k-tile of pair j (2j + kh, clamped: a prefetch past the end re-reads the
-  // last k-tile).
+  // this wave's k-tile of pair j (2j + kh, clamped: a prefetch past the end
+  // re-reads the last k-tile)
   const int KJ = (KT + 1) / 2;
-  auto load = [&](int j, v4u& w, uint32_t& h, v4u (&av)[kAPerThread]) {
-    const int kt_ = min(2 * j + kh, KT - 1);
-    const int ks = kt_ * kTileBytes, ka = kt_ * kBK;
+  auto ktile = [&](int j) { return min(2 * j + kh, KT - 1); };
+  // codes, coalesced (lane = tile row)
+  auto load_codes = [&](int j, v4u& w, uint32_t& h) {
+    const int ks = ktile(j) * kTileBytes;
     w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
     h = __builtin_amdgcn_raw_buffer_load_b32(rc, kTileHiOff + 4 * lane, ks, 0);
+  };
+  // this wave's share of the activation tile of pair j into buffer b
+  auto copy_a = [&](int j, int b) {
+    const int ka = ktile(j) * kBK;
+    int8_t* dst = a_buf(b) + 32 * wave * kBK;
 #pragma unroll
-    for (int i = 0; i < kAPerThread; ++i)
-      av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_v[i], ka, 0);
+    for (int jj = 0; jj < kACopies; ++jj)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(dst + 8 * jj * kBK), 16, a_v[jj], ka, 0, 0);
   };
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
-  // One k-step from one register stage; the stage is refilled with the
-  // loads for k-step kt+2 before the MFMAs.  The scheduling barriers keep
-  // the refill loads inside their own step, so every step finds exactly one
-  // newer stage in flight and waits only for its own.
-  auto step = [&](int j, v4u& w, uint32_t& h, v4u (&av)[kAPerThread]) {
-    int8_t* as = &As[(j & 1) * 2 + kh][0];
-    const bool live = 2 * j + kh < KT;     // odd KT: the last pair has one k-tile
-#pragma unroll
-    for (int i = 0; i < kAPerThread; ++i) *reinterpret_cast<v4u*>(as + a_lds[i]) = av[i];
-    // lane (l16, g) of block t <- dwords g (lo) and g+1 (hi) of row 16t+l16
+  // the 20-bit code groups of one register stage: lane (l16, g) of block t
+  // gets dwords g (lo) and g+1 (hi) of row 16t+l16, i.e. codes 8g..8g+3
+  // (sub-step 0) and 8g+4..8g+7 (sub-step 1)
+  auto split = [&](const v4u& w, uint32_t h, uint32_t (&f0)[kNT], uint32_t (&f1)[kNT]) {
     uint32_t lo[kNT], hi[kNT];
     transpose4(w.x, w.y, w.z, w.w, lo);
     transpose4(w.y, w.z, w.w, h, hi);
-    // codes 8g..8g+3 (sub-step 0) and 8g+4..8g+7 (sub-step 1), 20 bits each
-    uint32_t f0[kNT], f1[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
       const uint32_t x0 = __builtin_amdgcn_alignbit(hi[t], lo[t], sh);
       f0[t] = x0;
       f1[t] = __builtin_amdgcn_alignbit(hi[t] >> sh, x0, 20);
     }
-    load(min(j + 2, KJ - 1), w, h, av);
+  };
+  // Step j (activation buffer b = j % 3): its B operands bc0 / bc1 were
+  // decoded during step j-1; the register stage (wn, hn) holds the codes of
+  // step j+1, decoded during this step's MFMAs into bn0 / bn1 and then
+  // refilled with the codes of step j+3.
+  auto step = [&](int j, int b, v4u& wn, uint32_t& hn, const v4i (&bc0)[kNT], const v4i (&bc1)[kNT],
+                  v4i (&bn0)[kNT], v4i (&bn1)[kNT]) {
+    // every wave's copy of step j has landed and its earlier LDS reads are
+    // done; then the buffer of step j-1 is free for the copy of step j+2
     __builtin_amdgcn_sched_barrier(0);
-    v4i bop[kNT];
-    mg_decode(bop, f0, d2);      // the table is fixed: no wait for the barrier
-    lds_barrier();               // this pair's activations are in LDS
-    if (live) {
-      mg_mfma(acc, bop, as, l16, 2 * g);
-      mg_decode(bop, f1, d2);
-      mg_mfma(acc, bop, as, l16, 2 * g + 1);
-    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kNewerLoads));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     __builtin_amdgcn_sched_barrier(0);
+    copy_a(min(j + 2, KJ - 1), b == 0 ? 2 : b - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t f0[kNT], f1[kNT];
+    split(wn, hn, f0, f1);
+    load_codes(min(j + 3, KJ - 1), wn, hn);
+    __builtin_amdgcn_sched_barrier(0);
+    if (2 * j + kh < KT)     // odd KT: the last pair has one k-tile
+      mg_mfma<true>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
+    else
+      mg_mfma<false>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
   };
 
-  // two register stages, ping-pong: no register copies between k-steps
-  v4u w0, w1, av0[kAPerThread], av1[kAPerThread];
+  // Two register stages of codes and two sets of B operands, ping-pong.
+  // Issue order (the barrier's vmcnt counts on it): codes 0, copy 0,
+  // codes 1, copy 1, codes 2, then per step j: barrier, copy j+2,
+  // codes j+3.
+  v4u w0, w1;
   uint32_t h0, h1;
-  load(0, w0, h0, av0);
-  __builtin_amdgcn_sched_barrier(0);  // stage 0's loads strictly before stage 1's
-  load(min(1, KJ - 1), w1, h1, av1);
+  v4i bA0[kNT], bA1[kNT], bB0[kNT], bB1[kNT];
+  load_codes(0, w0, h0);
   __builtin_amdgcn_sched_barrier(0);
-  lds_barrier();  // decode table
-
-  int j = 0;
-  for (; j + 2 <= KJ; j += 2) {
-    step(j, w0, h0, av0);
-    step(j + 1, w1, h1, av1);
+  copy_a(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_codes(min(1, KJ - 1), w1, h1);
+  __builtin_amdgcn_sched_barrier(0);
+  copy_a(min(1, KJ - 1), 1);
+  __builtin_amdgcn_sched_barrier(0);
+  // decode table written (LDS only: the copies stay in flight)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    uint32_t f0[kNT], f1[kNT];
+    split(w0, h0, f0, f1);
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      bA0[t] = mg_decode4(f0[t], d2);
+      bA1[t] = mg_decode4(f1[t], d2);
+    }
+    load_codes(min(2, KJ - 1), w0, h0);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (j < KJ) step(j, w0, h0, av0);
 
-  // Epilogue, one 16-row block at a time: every wave writes its 16 x 64
-  // results (y = ((float)acc * s_x[m]) * alpha[n], or the raw int32) into a
-  // row-major LDS tile of 16 x 256, then the workgroup stores whole rows,
-  // 16 bytes per lane, so each store instruction writes full 128-byte lines.
-  // Lane (l16, g) of a 16 x 16 MFMA block holds column l16, rows 4g..4g+3.
-  uint32_t* ot = lds;   // [16][kOutLd] result words
+  int j = 0, b = 0;
+  for (; j + 2 <= KJ; j += 2) {
+    step(j, b, w1, h1, bA0, bA1, bB0, bB1);
+    b = b == 2 ? 0 : b + 1;
+    step(j + 1, b, w0, h0, bB0, bB1, bA0, bA1);
+    b = b == 2 ? 0 : b + 1;
+  }
+  if (j < KJ) step(j, b, w1, h1, bA0, bA1, bB0, bB1);
+  // the clamped copies past the end may still be landing in LDS, which the
+  // epilogue reuses
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+
+  // Epilogue, 32 rows (two row blocks) at a time: every wave writes its raw
+  // int32 sums into its parity's row-major LDS tile, then each thread adds
+  // the two parities for 4 consecutive columns of one row and stores
+  // y = ((float)acc * s_x[m]) * alpha[n] (or the int32 sum), 16 bytes per
+  // lane, so each store instruction writes whole 128-byte lines.  Lane
+  // (l16, g) of a 16 x 16 MFMA block holds column l16, rows 4g..4g+3.  The
+  // scales are read once, before the first barrier.
   const bool want_y = a.y != nullptr;
-  float al[kNT];
+  const int c4 = tid & (kBN / 4 - 1);          // this thread's 4 columns
+  const int n = n0 + 4 * c4;
+  float4 al4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (want_y && n < N) al4 = make_float4(a.alpha[n], a.alpha[n + 1], a.alpha[n + 2], a.alpha[n + 3]);
+  if (want_y && tid < kBM) sxs[tid] = a.s_x[min(m0 + tid, M - 1)];
+  int* ot0 = reinterpret_cast<int*>(lds);      // [32][kOutLd] sums of parity 0, then parity 1
+  int* ot1 = ot0 + 32 * kOutLd;
+  int* mine = kh == 0 ? ot0 : ot1;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t)
-    al[t] = want_y && n_live ? a.alpha[rt * kTileRows + 16 * t + l16] : 0.0f;
+  for (int qq = 0; qq < kMT / 2; ++qq) {
+    __syncthreads();  // the previous use of the LDS area is finished
 #pragma unroll
-  for (int i = 0; i < kMT; ++i) {
-    __syncthreads();  // previous use of the LDS area is finished
-    // the odd-parity waves hand their int32 sums to the even ones
-    if (kh == 1) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int t = 0; t < kNT; ++t)
-          ot[(4 * g + r) * kOutLd + wave * kTileRows + 16 * t + l16] = (uint32_t)acc[i][t][r];
-    }
-    __syncthreads();
-    if (kh == 0) {
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int t = 0; t < kNT; ++t)
-          acc[i][t][r] += (int)ot[(4 * g + r) * kOutLd + wave * kTileRows + 16 * t + l16];
-    }
+          mine[(16 * ii + 4 * g + r) * kOutLd + wave * kTileRows + 16 * t + l16] = acc[2 * qq + ii][t][r];
     __syncthreads();
-    if (kh == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int ml = 4 * g + r;                 // row within the block
-      const int m = min(m0 + 16 * i + ml, M - 1);
-      const float sx = want_y ? a.s_x[m] : 0.0f;
-#pragma unroll
-      for (int t = 0; t < kNT; ++t) {
-        const int col = wave * kTileRows + 16 * t + l16;
-        uint32_t v;
-        if (want_y) {
-          const float tv = (float)acc[i][t][r] * sx;
-          v = __builtin_bit_cast(uint32_t, tv * al[t]);
-        } else {
-          v = (uint32_t)acc[i][t][r];
-        }
-        ot[ml * kOutLd + col] = v;
-      }
-    }
-    }
-    __syncthreads();
-    // 16 rows x 64 float4 per block
-    for (int e = tid; e < 16 * (kBN / 4); e += kThreads) {
-      const int ml = e / (kBN / 4), c4 = e - ml * (kBN / 4);
-      const int m = m0 + 16 * i + ml, n = n0 + 4 * c4;
+    for (int k = 0; k < 32 * (kBN / 4) / kThreads; ++k) {
+      const int ml = tid / (kBN / 4) + (kThreads / (kBN / 4)) * k;   // row within the 32
+      const int m = m0 + 32 * qq + ml;
+      const v4i s0 = *reinterpret_cast<const v4i*>(&ot0[ml * kOutLd + 4 * c4]);
+      const v4i s1 = *reinterpret_cast<const v4i*>(&ot1[ml * kOutLd + 4 * c4]);
+      const v4i sum = s0 + s1;
       if (m < M && n < N) {
-        const v4u v = *reinterpret_cast<const v4u*>(&ot[ml * kOutLd + 4 * c4]);
-        void* dst = want_y ? static_cast<void*>(a.y + (size_t)m * N + n)
-                           : static_cast<void*>(a.acc + (size_t)m * N + n);
-        *reinterpret_cast<v4u*>(dst) = v;
+        if (want_y) {
+          const float sx = sxs[32 * qq + ml];
+          const float4 v = make_float4(((float)sum.x * sx) * al4.x, ((float)sum.y * sx) * al4.y,
+                                       ((float)sum.z * sx) * al4.z, ((float)sum.w * sx) * al4.w);
+          *reinterpret_cast<float4*>(a.y + (size_t)m * N + n) = v;
+        } else {
+          *reinterpret_cast<v4i*>(a.acc + (size_t)m * N + n) = sum;
+        }
       }
     }
   }
 }
 
 }  // namespace
+
+int mfma_gemm_lds_bytes() { return kLdsBytes + 1024 * 8 + kBM * 4; }
 
 int mfma_gemm_grid(int M, int N) {
   const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;

@@ -105,7 +105,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
     p.block = 512;
     p.splits = 1;
     p.kt_per_split = K / kTileK;
-    p.lds_bytes = 4 * 128 * kTileK + 1024 * 8;  // activation buffers + pair table
+    p.lds_bytes = mfma_gemm_lds_bytes();
     p.ws_bytes = 0;
     return p;
   }

@@ -60,6 +60,7 @@ bool mfma_gemv_fusable(const GemmPlan& plan, int M, int K);
 // The same GEMV on the 2-bit baseline format (packed = kTile2Bytes tiles).
 hipError_t launch_mfma_gemv2(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 int mfma_gemm_grid(int M, int N);
+int mfma_gemm_lds_bytes();
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 
 }  // namespace sherry
