@@ -7,9 +7,11 @@
 // for W4A8 (xllm-io page, FastGEMM section).
 //
 // Workgroup tile: BM = 128 activation rows x BN = 256 weight rows (4 format
-// row tiles), k-steps of one format k-tile (128 inputs); 4 waves, one per
-// SIMD.  Wave w owns row tile w, i.e. 64 weight rows = 4 MFMA column blocks,
-// against all 128 activation rows = 8 MFMA row blocks (8 x 4 accumulators).
+// row tiles), k-steps of one format k-tile (128 inputs); 8 waves, two per
+// SIMD: wave (kh, w) takes the k-tiles of parity kh (2j + kh) of row tile w,
+// i.e. 64 weight rows = 4 MFMA column blocks, against all 128 activation
+// rows = 8 MFMA row blocks (8 x 4 accumulators); the two parities' sums are
+// added in the epilogue.
 // A decoded weight operand therefore feeds 8 MFMAs and an activation
 // fragment 4, which keeps the LDS work per k-tile (pair-table lookups plus
 // activation fragments) well below the matrix-core time.
@@ -365,6 +367,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
 }  // namespace
 
 int mfma_gemm_lds_bytes() { return kLdsBytes + 1024 * 8 + kBM * 4; }
+
+int mfma_gemm_threads() { return kThreads; }
 
 int mfma_gemm_grid(int M, int N) {
   const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;

@@ -102,7 +102,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
   if (M > kLutMaxM) {
     p.path = 1;
     p.grid = mfma_gemm_grid(M, N);
-    p.block = 512;
+    p.block = mfma_gemm_threads();
     p.splits = 1;
     p.kt_per_split = K / kTileK;
     p.lds_bytes = mfma_gemm_lds_bytes();

@@ -61,6 +61,7 @@ bool mfma_gemv_fusable(const GemmPlan& plan, int M, int K);
 hipError_t launch_mfma_gemv2(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 int mfma_gemm_grid(int M, int N);
 int mfma_gemm_lds_bytes();
+int mfma_gemm_threads();
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 
 }  // namespace sherry
