@@ -91,6 +91,15 @@ __device__ __forceinline__ float amax4(const float4 v) {
   return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+// Activations of 16-token blocks are loaded four lanes per row (lane
+// 4r + g: token r, inputs 32g..32g+31), so each group of four lanes reads
+// one 128-byte line, and moved to the MFMA layout (lane 16g + r) by LDS
+// crossbar permutes; token-per-lane loads put four lines under every four
+// lanes.  Measured at N=14336, K=4096: M=16 7.9 -> 7.8 us, M=32 10.2 -> 8.9,
+// M=64 16.6 -> 12.6; for 8-token blocks the permutes cost more than they
+// save (M=8, K=8192, N=28672: 14.0 -> 15.6 us), so those keep the direct form.
+constexpr bool quad_x(int MT, int MB) { return MT == 16 && MB >= 1; }
+
 // KW waves share one row tile; MT = the token count of one MFMA token block
 // rounded up to a power of two (1..16); MB = token blocks of 16 (MB > 1 only
 // with MT = 16: up to 64 tokens, each decoded code feeding MB instructions);
@@ -101,6 +110,7 @@ __device__ __forceinline__ float amax4(const float4 v) {
 template <int KW, int MT, int MB, bool FQ, int FMT, int ST>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int splits, int kt_per_split) {
   static_assert(MB == 1 || (MT == 16 && !FQ), "several token blocks are whole blocks of 16");
+  constexpr bool XQ = !FQ && quad_x(MT, MB);
   constexpr int kStages = ST;
   constexpr int NT = 64 * KW;
   constexpr int TB = FMT == 0 ? kTileBytes : kTile2Bytes;   // bytes per format tile
@@ -132,7 +142,8 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   // lane offset of the activations (>= M*K for the padding tokens; the
   // k-tile offset is added to it, not passed as the scalar offset, so the
   // descriptor's range check sees the whole offset)
-  const int x_v = l16 * K + 32 * g;
+  const int x_v = XQ ? (lane >> 2) * K + 32 * (lane & 3) : l16 * K + 32 * g;
+  const int xq_src = 4 * (4 * l16 + g);       // permute address: lane 16g + r <- lane 4r + g
   const uint32_t sh = 8u * (uint32_t)g;      // bit 40g mod 32
 
   // i-th k-tile of this wave (clamped: the prefetch past the end re-reads
@@ -260,6 +271,13 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
       for (int b = 0; b < MB; ++b) {
         a0[b] = __builtin_bit_cast(v4i, x0[b]);
         a1[b] = __builtin_bit_cast(v4i, x1[b]);
+        if constexpr (XQ) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            a0[b][d] = __builtin_amdgcn_ds_bpermute(xq_src, a0[b][d]);
+            a1[b][d] = __builtin_amdgcn_ds_bpermute(xq_src, a1[b][d]);
+          }
+        }
       }
     }
     load(i + kStages, w, h, x0, x1);
