@@ -95,25 +95,30 @@ void set_plan_override(int path, int rw, int ch, int splits) {
   g_ovr_splits = splits;
 }
 
+namespace {
+// Prefill GEMM: one workgroup per 128 x 256 output tile, no K-split.
+GemmPlan plan_prefill(int M, int N, int K) {
+  GemmPlan p{};
+  p.path = 1;
+  p.grid = mfma_gemm_grid(M, N);
+  p.block = mfma_gemm_threads();
+  p.splits = 1;
+  p.kt_per_split = K / kTileK;
+  p.lds_bytes = mfma_gemm_lds_bytes();
+  p.ws_bytes = 0;
+  return p;
+}
+}  // namespace
+
+// M <= 16: the built-in small-M path (or the override's); 16 < M <= 64: the
+// matrix-core GEMV unless the prefill kernel is forced; M > 64: prefill.
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   const int ovr = g_ovr_path.load();
-  if (M > kLutMaxM && M <= kGemvMaxM && ovr != 1) return plan_mfma_gemv(M, N, K);
-  if (M > kLutMaxM) {
-    p.path = 1;
-    p.grid = mfma_gemm_grid(M, N);
-    p.block = mfma_gemm_threads();
-    p.splits = 1;
-    p.kt_per_split = K / kTileK;
-    p.lds_bytes = mfma_gemm_lds_bytes();
-    p.ws_bytes = 0;
-    return p;
-  }
+  if (M > kGemvMaxM || (M > kLutMaxM && ovr == 1)) return plan_prefill(M, N, K);
+  if (M > kLutMaxM) return plan_mfma_gemv(M, N, K);
   const int path = ovr >= 0 ? ovr : kDefaultSmallMPath;
-  if (path == 1) {
-    GemmPlan q = plan_gemm(kLutMaxM + 1, N, K);
-    return q;
-  }
+  if (path == 1) return plan_prefill(M, N, K);
   if (path == 2) return plan_mfma_gemv(M, N, K);
   const int MP = (M + 1) / 2;
   const int KT = K / kTileK;

@@ -104,12 +104,17 @@ sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
  *   workspace / workspace_bytes: scratch of at least
  *            sherry_workspace_bytes(M,N,K) bytes, 256-byte aligned, zero
  *            filled before first use (may be NULL when that size is 0).
- * M > 16 decodes the codes to int8 {-1,0,+1} and contracts them on int8
- * matrix cores (workgroup tiles of 64 x 448 outputs).  M <= 16 runs either
- * the lookup-table GEMV (per-segment tables of the 16 pattern dot products
- * and their negations in LDS, one lookup per weight block and token pair) or
- * the same decode + matrix-core contraction with the tokens padded to 16;
- * sherry_gemm_plan reports which.  Every path returns identical results. */
+ * Every path decodes the codes or looks them up; which one runs depends on
+ * M (sherry_gemm_plan reports it), and every path returns identical results:
+ *   M <= 16: the matrix-core GEMV (codes decoded to int8 {-1,0,+1}, tokens
+ *            padded to 16, one 64-row weight tile per workgroup), or the
+ *            lookup-table GEMV (per-segment tables of the 16 pattern dot
+ *            products and their negations in LDS, one lookup per weight
+ *            block and token pair);
+ *   16 < M <= 64: the matrix-core GEMV with the tokens in two or four
+ *            blocks of 16;
+ *   M > 64:  the prefill GEMM (workgroup tiles of 128 tokens x 256 weight
+ *            rows on the int8 matrix cores). */
 sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           const float* alpha, float* y, int64_t M, int64_t N,
                           int64_t K, void* workspace, size_t workspace_bytes,
@@ -177,9 +182,9 @@ sherry_status sherry_gemm2(const int8_t* x, const float* s_x, const void* packed
 
 /* Launch plan sherry_gemm uses for a shape (host-only, pure; for
  * diagnostics and benchmarks).  Any output pointer may be NULL.
- *   path: 0 = lookup-table GEMV (per-segment tables in LDS, §2.2),
- *         1 = decode + int8 matrix-core GEMM (the M > 16 path),
- *         2 = decode + int8 matrix-core GEMV (M <= 16).
+ *   path: 0 = lookup-table GEMV (per-segment tables in LDS, §2.2; M <= 16),
+ *         1 = decode + int8 matrix-core GEMM (the M > 64 path),
+ *         2 = decode + int8 matrix-core GEMV (M <= 64).
  *   grid: workgroups per launch; block: threads per workgroup;
  *   splits: K-splits per output row group (1 = none);
  *   lds_bytes: LDS per workgroup. */
@@ -188,13 +193,15 @@ sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path,
                                int* lds_bytes);
 
 /* Tuning knob for benchmark sweeps and tests (host-only).  Replaces the
- * built-in launch plan for shapes with M <= 16 for every later call in this
- * process (M > 16 always uses path 1):
- *   path   -1 = built-in choice, or 0, 1, 2 as in sherry_gemm_plan.
+ * built-in launch plan for shapes with M <= 64 for every later call in this
+ * process (M > 64 always uses path 1):
+ *   path   -1 = built-in choice, or 0, 1, 2 as in sherry_gemm_plan; for
+ *          16 < M <= 64 only 1 changes the path (0 and 2 give path 2).
  *   rw     path 0: row tiles per workgroup, 1, 2 or 4 (the workgroup's 4
  *          waves are rw row tiles x 4/rw waves sharing one);
  *          path 2: waves per workgroup sharing its one row tile, 4, 8 or
- *          16; 0 (or a value the path does not take) = built-in choice.
+ *          16 (at most 8 when M > 16); 0 (or a value the path does not
+ *          take) = built-in choice.
  *   ch     path 0 only: k-tiles (128 inputs) per LDS table stage: 1, 2, 4
  *          or 8, capped so one stage stays within 32 KB; 0 = built-in.
  *   splits K-splits per output row group; 0 = built-in choice.
