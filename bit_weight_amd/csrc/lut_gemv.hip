@@ -28,6 +28,13 @@
 //    arrivals, the low word is the exact int32 sum.  The split that brings
 //    the count to `splits` writes the output and stores the zero back, so
 //    the reduction costs one memory round trip and no cache maintenance.
+//  * Fused form (FQ, sherry_linear with M <= 4): the activations arrive as
+//    fp32.  Every workgroup first reads its tokens' whole rows for the
+//    per-token scale s = max|x| / 127, and the table builder quantizes the
+//    4 inputs of its segment as it reads them, q = clamp(rint(x / s), +-127),
+//    with the stand-alone quantizer's arithmetic, so q, the tables and y are
+//    bit-identical to quantizing first; the quantizer's launch and the round
+//    trip of q through memory are saved.
 #include "sherry_device.h"
 #include "sherry_launch.h"
 
@@ -36,17 +43,34 @@ namespace {
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
 
+// Four fp32 activations quantized with scale s into the 4 int8 lanes of a
+// dword (byte j = input j).
+__device__ __forceinline__ int quant_word(const float* x, float s) {
+  const float4 v = *reinterpret_cast<const float4*>(x);
+  const uint32_t b0 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.x / s), -127.0f), 127.0f);
+  const uint32_t b1 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.y / s), -127.0f), 127.0f);
+  const uint32_t b2 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.z / s), -127.0f), 127.0f);
+  const uint32_t b3 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.w / s), -127.0f), 127.0f);
+  return (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+}
+
+__device__ __forceinline__ float amax4(const float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
 __device__ __forceinline__ short2_t pair_of(int x0, int x1, int j) {
   // int8 activation j of two tokens' segment words, widened to int16 halves
   return short2_t{(short)(int8_t)(x0 >> (8 * j)), (short)(int8_t)(x1 >> (8 * j))};
 }
 
-template <int MP, int CH, int RW, int KW>
+template <int MP, int CH, int RW, int KW, bool FQ>
 __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int splits,
                                                                  int kt_per_split) {
   constexpr int NT = 64 * RW * KW;
   constexpr int CPW = (CH + KW - 1) / KW;        // k-tiles per wave per stage
-  extern __shared__ uint32_t lut[];               // tables start at LDS 0
+  extern __shared__ uint32_t lut[];               // tables (dynamic LDS)
+  __shared__ float fq_red[FQ ? RW * KW * 2 * MP : 1];   // fused form: partial maxima
+  __shared__ float fq_s[FQ ? 2 * MP : 1];               //   and the per-token scales
 
   const int M = a.M, N = a.N, K = a.K;
   const int KT = K / kTileK, RT = N / kTileRows;
@@ -80,6 +104,31 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
   uint32_t cur[CPW][5];
   load_stage(0, cur);
 
+  if constexpr (FQ) {
+    // per-token scale over the whole row (every workgroup reads its tokens'
+    // rows), s = max|x| / 127, an all-zero row -> 1
+    const int K4 = K / 4;
+#pragma unroll
+    for (int m = 0; m < 2 * MP; ++m) {
+      float am = 0.0f;
+      if (m < M) {
+        const float4* xr = reinterpret_cast<const float4*>(a.xf + (size_t)m * K);
+#pragma unroll 4
+        for (int e = threadIdx.x; e < K4; e += NT) am = fmaxf(am, amax4(xr[e]));
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      if (lane == 0) fq_red[wave * 2 * MP + m] = am;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2 * MP) {
+      float v = 0.0f;
+      for (int w = 0; w < RW * KW; ++w) v = fmaxf(v, fq_red[w * 2 * MP + threadIdx.x]);
+      fq_s[threadIdx.x] = !(v > 0.0f) ? 1.0f : v / 127.0f;
+    }
+    __syncthreads();
+  }
+
   int acc[2 * MP];
 #pragma unroll
   for (int m = 0; m < 2 * MP; ++m) acc[m] = 0;
@@ -99,8 +148,14 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
         const int seg = rest / MP;
         const int k = kt_s * kTileK + 4 * seg;
         const int m0 = 2 * pair, m1 = 2 * pair + 1;
-        const int x0 = m0 < M ? *reinterpret_cast<const int*>(a.x + (size_t)m0 * K + k) : 0;
-        const int x1 = m1 < M ? *reinterpret_cast<const int*>(a.x + (size_t)m1 * K + k) : 0;
+        int x0 = 0, x1 = 0;
+        if constexpr (FQ) {
+          if (m0 < M) x0 = quant_word(a.xf + (size_t)m0 * K + k, fq_s[m0]);
+          if (m1 < M) x1 = quant_word(a.xf + (size_t)m1 * K + k, fq_s[m1]);
+        } else {
+          if (m0 < M) x0 = *reinterpret_cast<const int*>(a.x + (size_t)m0 * K + k);
+          if (m1 < M) x1 = *reinterpret_cast<const int*>(a.x + (size_t)m1 * K + k);
+        }
         // the three kept positions in order: ja < jb < jc, none equal to z
         const int ja = z == 0 ? 1 : 0;
         const int jb = z <= 1 ? 2 : 1;
@@ -212,7 +267,7 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
   for (int m = 0; m < 2 * MP; ++m) {
     if (m >= M || !last[m]) continue;
     if (a.y) {
-      const float t = (float)total[m] * a.s_x[m];
+      const float t = (float)total[m] * (FQ ? fq_s[m] : a.s_x[m]);
       a.y[(size_t)m * N + n] = t * al;
     } else {
       a.acc[(size_t)m * N + n] = total[m];
@@ -220,30 +275,30 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
   }
 }
 
-template <int MP, int CH, int RW, int KW>
+template <int MP, int CH, int RW, int KW, bool FQ>
 hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((lut_gemv_kernel<MP, CH, RW, KW>), dim3(p.grid), dim3(64 * RW * KW),
+  hipLaunchKernelGGL((lut_gemv_kernel<MP, CH, RW, KW, FQ>), dim3(p.grid), dim3(64 * RW * KW),
                      p.lds_bytes, stream, a, p.splits, p.kt_per_split);
   return hipGetLastError();
 }
 
-template <int MP, int CH>
+template <int MP, int CH, bool FQ>
 hipError_t launch_ch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   switch (p.rw) {
-    case 4: return launch_cfg<MP, CH, 4, 1>(p, a, stream);
-    case 2: return launch_cfg<MP, CH, 2, 2>(p, a, stream);
-    case 1: return launch_cfg<MP, CH, 1, 4>(p, a, stream);
+    case 4: return launch_cfg<MP, CH, 4, 1, FQ>(p, a, stream);
+    case 2: return launch_cfg<MP, CH, 2, 2, FQ>(p, a, stream);
+    case 1: return launch_cfg<MP, CH, 1, 4, FQ>(p, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int MP>
+template <int MP, bool FQ>
 hipError_t launch_mp(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   switch (p.ch) {
-    case 1: return launch_ch<MP, 1>(p, a, stream);
-    case 2: return launch_ch<MP, 2>(p, a, stream);
-    case 4: if constexpr (MP <= 4) return launch_ch<MP, 4>(p, a, stream); break;
-    case 8: if constexpr (MP <= 2) return launch_ch<MP, 8>(p, a, stream); break;
+    case 1: return launch_ch<MP, 1, FQ>(p, a, stream);
+    case 2: return launch_ch<MP, 2, FQ>(p, a, stream);
+    case 4: if constexpr (MP <= 4) return launch_ch<MP, 4, FQ>(p, a, stream); break;
+    case 8: if constexpr (MP <= 2) return launch_ch<MP, 8, FQ>(p, a, stream); break;
     default: break;
   }
   return hipErrorInvalidValue;
@@ -251,16 +306,29 @@ hipError_t launch_mp(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// The fused form takes up to kFuseMaxM tokens whose rows (M*K fp32) every
+// workgroup reads once.
+bool lut_gemv_fusable(const GemmPlan& p, int M, int K) {
+  return p.path == 0 && M <= kFuseMaxM && (long long)M * K <= kFuseMaxMK;
+}
+
 hipError_t launch_lut_gemv(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  if (a.xf) {
+    switch ((a.M + 1) / 2) {
+      case 1: return launch_mp<1, true>(p, a, stream);
+      case 2: return launch_mp<2, true>(p, a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch ((a.M + 1) / 2) {
-    case 1: return launch_mp<1>(p, a, stream);
-    case 2: return launch_mp<2>(p, a, stream);
-    case 3: return launch_mp<3>(p, a, stream);
-    case 4: return launch_mp<4>(p, a, stream);
-    case 5: return launch_mp<5>(p, a, stream);
-    case 6: return launch_mp<6>(p, a, stream);
-    case 7: return launch_mp<7>(p, a, stream);
-    case 8: return launch_mp<8>(p, a, stream);
+    case 1: return launch_mp<1, false>(p, a, stream);
+    case 2: return launch_mp<2, false>(p, a, stream);
+    case 3: return launch_mp<3, false>(p, a, stream);
+    case 4: return launch_mp<4, false>(p, a, stream);
+    case 5: return launch_mp<5, false>(p, a, stream);
+    case 6: return launch_mp<6, false>(p, a, stream);
+    case 7: return launch_mp<7, false>(p, a, stream);
+    case 8: return launch_mp<8, false>(p, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -201,7 +201,7 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // not fused into the product (any content; not kept zero).
 size_t linear_scratch(int M, int N, int K, GemmPlan* plan_out, bool* fused_out) {
   const GemmPlan plan = plan_gemm(M, N, K);
-  const bool fused = mfma_gemv_fusable(plan, M, K);
+  const bool fused = mfma_gemv_fusable(plan, M, K) || lut_gemv_fusable(plan, M, K);
   if (plan_out) *plan_out = plan;
   if (fused_out) *fused_out = fused;
   return fused ? 0 : round256((size_t)M * K) + round256((size_t)M * 4);
@@ -381,7 +381,7 @@ sherry_status sherry_linear(const float* x, const void* packed, const float* alp
   hipError_t e;
   if (fused) {
     args.xf = x;
-    e = launch_mfma_gemv(plan, args, st);
+    e = plan.path == 0 ? launch_lut_gemv(plan, args, st) : launch_mfma_gemv(plan, args, st);
   } else {
     int8_t* q = static_cast<int8_t*>(scratch);
     float* s_x = reinterpret_cast<float*>(q + round256((size_t)M * K));

@@ -57,6 +57,7 @@ hipError_t launch_quantize_act(const float* x, int M, int K, int8_t* q, float* s
 hipError_t launch_lut_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 hipError_t launch_mfma_gemv(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 bool mfma_gemv_fusable(const GemmPlan& plan, int M, int K);
+bool lut_gemv_fusable(const GemmPlan& plan, int M, int K);
 // The same GEMV on the 2-bit baseline format (packed = kTile2Bytes tiles).
 hipError_t launch_mfma_gemv2(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 int mfma_gemm_grid(int M, int N);

@@ -161,6 +161,14 @@ def test_linear_scratch_and_validation():
     L = bw.lib()
     # fused (M <= 4, M*K <= 16384): no scratch
     assert bw.linear_scratch_bytes(1, 4096, 4096) == 0
+    try:   # the lookup-table path fuses the quantization under the same limits
+        bw.plan_override("lut_gemv")
+        assert bw.linear_scratch_bytes(1, 4096, 4096) == 0
+        assert bw.linear_scratch_bytes(4, 4096, 4096) == 0
+        assert bw.linear_scratch_bytes(5, 4096, 4096) == 5 * 4096 + 256
+        assert bw.linear_scratch_bytes(2, 4096, 11008) == 2 * 11008 + 256   # M*K > 16384
+    finally:
+        bw.plan_override()
     # not fused: q [M,K] + s_x [M], each rounded up to 256 bytes
     assert bw.linear_scratch_bytes(16, 4096, 4096) == 16 * 4096 + 256
     assert bw.linear_scratch_bytes(512, 14336, 4096) == 512 * 4096 + 2048

@@ -295,10 +295,12 @@ def test_linear_edges(orc, packed_cases, M, N, K):
 
 @pytest.mark.parametrize("path,rw,splits", [("decode_mfma_gemv", 4, 1), ("decode_mfma_gemv", 4, 3),
                                             ("decode_mfma_gemv", 16, 2), ("decode_mfma_gemv", 8, 9),
-                                            ("lut_gemv", 0, 0), ("decode_mfma", 0, 0)])
-@pytest.mark.parametrize("M", [1, 4])
+                                            ("lut_gemv", 0, 0), ("lut_gemv", 1, 3), ("lut_gemv", 2, 1),
+                                            ("lut_gemv", 4, 9), ("decode_mfma", 0, 0)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_linear_plans(orc, packed_cases, path, rw, splits, M):
-    """Fused (matrix-core GEMV) and unfused (other paths) forms agree."""
+    """Fused (both GEMVs) and unfused (prefill kernel) forms agree with the
+    oracle and with quantize + product, at every launch shape."""
     N, K = 320, 1152
     T, alpha, packed, galpha = packed_cases[(N, K)]
     x = synth.activations(M, K, seed=4100 + M, outlier_channels=True)
@@ -320,6 +322,24 @@ def test_linear_workloads(orc, name):
     del W
     _say(f"linear workload {w.description} scratch={bw.linear_scratch_bytes(w.M, w.N, w.K)}")
     _linear_check(orc, x, packed, T, alpha, galpha, w.N, w.K, name)
+
+
+@pytest.mark.parametrize("name", ["1", "2a", "2b", "3a", "3b"])
+def test_linear_workloads_lut_fused(orc, name):
+    """The lookup-table GEMV with the quantization fused in, at full size."""
+    w = synth.WORKLOADS[name]
+    W = synth.workload_weights(w)
+    x = synth.workload_activations(w)
+    T, alpha = orc.quantize(W.numpy())
+    packed, galpha = gpu_pack(W)
+    del W
+    try:
+        bw.plan_override("lut_gemv")
+        assert bw.linear_scratch_bytes(w.M, w.N, w.K) == 0          # fused
+        _say(f"linear workload {w.description} on the LUT path: {bw.plan(w.M, w.N, w.K)}")
+        _linear_check(orc, x, packed, T, alpha, galpha, w.N, w.K, name)
+    finally:
+        bw.plan_override()
 
 
 def test_grouped_projections_one_call(orc):
