@@ -132,7 +132,7 @@ PATH_IDS = {v: k for k, v in PATHS.items()}
 
 
 def plan_override(path=None, rw: int = 0, ch: int = 0, splits: int = 0) -> None:
-    """Tuning knob for M <= 64: force a path ("lut_gemv", "decode_mfma",
+    """Tuning knob for M <= 128: force a path ("lut_gemv", "decode_mfma",
     "decode_mfma_gemv" or None = built-in) and its launch plan (0 = built-in).
     Above M = 16 only "decode_mfma" changes the path."""
     pid = -1 if path is None else PATH_IDS[path]

@@ -95,6 +95,28 @@ void set_plan_override(int path, int rw, int ch, int splits) {
   g_ovr_splits = splits;
 }
 
+hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream) {
+  auto one = [&](const GemmArgs& a) {
+    return plan.path == 0   ? launch_lut_gemv(plan, a, stream)
+           : plan.path == 2 ? launch_mfma_gemv(plan, a, stream)
+                            : launch_mfma_gemm(plan, a, stream);
+  };
+  if (plan.chunk <= 0 || args.M <= plan.chunk) return one(args);
+  // launches of plan.chunk tokens in stream order; each leaves the split-K
+  // workspace zero for the next
+  for (int m0 = 0; m0 < args.M; m0 += plan.chunk) {
+    GemmArgs c = args;
+    c.M = args.M - m0 < plan.chunk ? args.M - m0 : plan.chunk;
+    c.x = args.x + (size_t)m0 * args.K;
+    if (args.s_x) c.s_x = args.s_x + m0;
+    if (args.y) c.y = args.y + (size_t)m0 * args.N;
+    if (args.acc) c.acc = args.acc + (size_t)m0 * args.N;
+    const hipError_t e = one(c);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 namespace {
 // Prefill GEMM: one workgroup per 128 x 256 output tile, no K-split.
 GemmPlan plan_prefill(int M, int N, int K) {
@@ -111,11 +133,19 @@ GemmPlan plan_prefill(int M, int N, int K) {
 }  // namespace
 
 // M <= 16: the built-in small-M path (or the override's); 16 < M <= 64: the
-// matrix-core GEMV unless the prefill kernel is forced; M > 64: prefill.
+// matrix-core GEMV unless the prefill kernel is forced; 64 < M <= 128: the
+// same GEMV in launches of 64 tokens (each streams the weights again: M=128
+// takes 2 x 12.5 us at N=14336, K=4096, where the prefill kernel's 56-112
+// tiles take 30-32 us); M > 128: prefill.
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   const int ovr = g_ovr_path.load();
-  if (M > kGemvMaxM || (M > kLutMaxM && ovr == 1)) return plan_prefill(M, N, K);
+  if (M > kChunkMaxM || (M > kLutMaxM && ovr == 1)) return plan_prefill(M, N, K);
+  if (M > kGemvMaxM) {   // two launches of the 64-token GEMV beat the few prefill tiles here
+    GemmPlan c = plan_mfma_gemv(kGemvMaxM, N, K);
+    c.chunk = kGemvMaxM;
+    return c;
+  }
   if (M > kLutMaxM) return plan_mfma_gemv(M, N, K);
   const int path = ovr >= 0 ? ovr : kDefaultSmallMPath;
   if (path == 1) return plan_prefill(M, N, K);
@@ -189,9 +219,7 @@ sherry_status run_gemm(const int8_t* x, const float* s_x, const void* packed, co
   args.K = (int)K;
   if (plan.ws_bytes > 0) args.partials = static_cast<int32_t*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = plan.path == 0   ? launch_lut_gemv(plan, args, s)
-                       : plan.path == 2 ? launch_mfma_gemv(plan, args, s)
-                                        : launch_mfma_gemm(plan, args, s);
+  const hipError_t e = launch_product(plan, args, s);
   return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
 }
 
@@ -389,9 +417,7 @@ sherry_status sherry_linear(const float* x, const void* packed, const float* alp
     if (e == hipSuccess) {
       args.x = q;
       args.s_x = s_x;
-      e = plan.path == 0   ? launch_lut_gemv(plan, args, st)
-          : plan.path == 2 ? launch_mfma_gemv(plan, args, st)
-                           : launch_mfma_gemm(plan, args, st);
+      e = launch_product(plan, args, st);
     }
   }
   return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;

@@ -20,10 +20,12 @@ struct GemmPlan {
   int groups;        // output row groups (GEMV)
   int lds_bytes;     // dynamic LDS per workgroup
   size_t ws_bytes;   // workspace bytes required
+  int chunk;         // tokens per launch (0 = all M in one launch)
 };
 
 constexpr int kLutMaxM = 16;          // M <= 16 takes a GEMV path
 constexpr int kGemvMaxM = 64;         // 16 < M <= 64: the matrix-core GEMV, unless path 1 is forced
+constexpr int kChunkMaxM = 128;       // 64 < M <= 128: the GEMV in launches of 64 tokens
 constexpr int kGemvWaves = 4;         // waves per GEMV workgroup
 constexpr int kDefaultSmallMPath = 2;  // M <= 16: 0 = lookup tables, 2 = matrix-core GEMV
 constexpr int kFuseMaxM = 4;           // fused quantization: at most 4 tokens,
@@ -64,5 +66,8 @@ int mfma_gemm_grid(int M, int N);
 int mfma_gemm_lds_bytes();
 int mfma_gemm_threads();
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
+// The product (x int8) on the plan's path, in launches of plan.chunk tokens
+// when the plan asks for it.
+hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 
 }  // namespace sherry

@@ -113,7 +113,9 @@ sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
  *            block and token pair);
  *   16 < M <= 64: the matrix-core GEMV with the tokens in two or four
  *            blocks of 16;
- *   M > 64:  the prefill GEMM (workgroup tiles of 128 tokens x 256 weight
+ *   64 < M <= 128: that GEMV in launches of 64 tokens on the same stream
+ *            (sherry_workspace_bytes covers one launch);
+ *   M > 128: the prefill GEMM (workgroup tiles of 128 tokens x 256 weight
  *            rows on the int8 matrix cores). */
 sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           const float* alpha, float* y, int64_t M, int64_t N,
@@ -183,8 +185,9 @@ sherry_status sherry_gemm2(const int8_t* x, const float* s_x, const void* packed
 /* Launch plan sherry_gemm uses for a shape (host-only, pure; for
  * diagnostics and benchmarks).  Any output pointer may be NULL.
  *   path: 0 = lookup-table GEMV (per-segment tables in LDS, §2.2; M <= 16),
- *         1 = decode + int8 matrix-core GEMM (the M > 64 path),
- *         2 = decode + int8 matrix-core GEMV (M <= 64).
+ *         1 = decode + int8 matrix-core GEMM (the M > 128 path),
+ *         2 = decode + int8 matrix-core GEMV (M <= 128; grid is per launch
+ *             of at most 64 tokens).
  *   grid: workgroups per launch; block: threads per workgroup;
  *   splits: K-splits per output row group (1 = none);
  *   lds_bytes: LDS per workgroup. */
@@ -193,10 +196,10 @@ sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path,
                                int* lds_bytes);
 
 /* Tuning knob for benchmark sweeps and tests (host-only).  Replaces the
- * built-in launch plan for shapes with M <= 64 for every later call in this
- * process (M > 64 always uses path 1):
+ * built-in launch plan for shapes with M <= 128 for every later call in this
+ * process (M > 128 always uses path 1):
  *   path   -1 = built-in choice, or 0, 1, 2 as in sherry_gemm_plan; for
- *          16 < M <= 64 only 1 changes the path (0 and 2 give path 2).
+ *          16 < M <= 128 only 1 changes the path (0 and 2 give path 2).
  *   rw     path 0: row tiles per workgroup, 1, 2 or 4 (the workgroup's 4
  *          waves are rw row tiles x 4/rw waves sharing one);
  *          path 2: waves per workgroup sharing its one row tile, 4, 8 or

@@ -54,7 +54,10 @@ def test_plan_dispatch_rule():
     for M in (17, 31, 64):
         p = bw.plan(M, 4096, 4096)
         assert p["path"] == "decode_mfma_gemv" and p["block"] <= 512   # at most 8 waves
-    for M in (65, 130, 512):
+    for M in (65, 100, 128):   # launches of 64 tokens on the GEMV
+        assert bw.plan(M, 4096, 4096)["path"] == "decode_mfma_gemv"
+        assert bw.workspace_bytes(M, 4096, 4096) in (0, 64 * 4096 * 8)
+    for M in (129, 130, 512):
         assert bw.plan(M, 4096, 4096)["path"] == "decode_mfma"
     p = bw.plan(1, 4096, 4096)
     assert p["block"] in (256, 512, 1024) and p["grid"] >= 64
@@ -86,11 +89,13 @@ def test_plan_override_changes_plan_and_workspace():
         assert bw.workspace_bytes(2, 4096, 4096) == 0
         assert bw.plan(40, 4096, 4096)["path"] == "decode_mfma"   # forced on 16 < M <= 64 too
         assert bw.plan(100, 4096, 4096)["path"] == "decode_mfma"
+        assert bw.plan(200, 4096, 4096)["path"] == "decode_mfma"
         bw.plan_override("lut_gemv")
         assert bw.plan(40, 4096, 4096)["path"] == "decode_mfma_gemv"   # no table path above 16
         bw.plan_override("decode_mfma_gemv", rw=16)
         assert bw.plan(40, 4096, 4096)["block"] == 512
-        assert bw.plan(100, 4096, 4096)["path"] == "decode_mfma"
+        assert bw.plan(100, 4096, 4096)["path"] == "decode_mfma_gemv"
+        assert bw.plan(129, 4096, 4096)["path"] == "decode_mfma"
         with pytest.raises(bw.SherryError):
             bw.plan_override("lut_gemv", rw=3)
         assert bw.lib().sherry_gemm_plan_override(3, 0, 0, 0) == SHAPE

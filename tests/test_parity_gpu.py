@@ -96,7 +96,7 @@ def test_act_quant_ties_golden(orc):
 
 # ----------------------------------------------------- product, edge shapes
 SHAPES = [(64, 128), (192, 384), (320, 1152)]
-MS = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 64, 130]
+MS = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 64, 65, 100, 128, 129, 130]
 
 
 @pytest.fixture(scope="module")
@@ -153,12 +153,13 @@ GEMV_PLANS = [(4, 0), (4, 1), (4, 2), (4, 3), (4, 9), (8, 0), (8, 1), (8, 2), (1
 
 
 @pytest.mark.parametrize("rw,splits", GEMV_PLANS)
-@pytest.mark.parametrize("M", [1, 2, 5, 8, 13, 16, 17, 31, 32, 33, 50, 64])
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 13, 16, 17, 31, 32, 33, 50, 64, 65, 97, 128])
 @pytest.mark.parametrize("N,K", [(320, 1152), (64, 128)])
 def test_gemm_mfma_gemv_plans(orc, packed_cases, rw, splits, M, N, K):
     """Every launch shape of the small-M matrix-core GEMV (waves per row tile
     incl. idle ones, K-splits incl. ragged ones, one to four token blocks of
-    16 with a ragged last block) gives the same exact result, and the fp32
+    16 with a ragged last block, launches of 64 tokens above M = 64 that
+    share the split-K workspace) gives the same exact result, and the fp32
     output matches the oracle."""
     T, alpha, packed, galpha = packed_cases[(N, K)]
     q = synth.int8_uniform(M, K, seed=1900 + M + K)
@@ -176,7 +177,7 @@ def test_gemm_mfma_gemv_plans(orc, packed_cases, rw, splits, M, N, K):
     assert_y_close(gy.cpu().numpy(), y)
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64])
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64, 100, 128])
 def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M):
     """The prefill kernel forced onto a small M (rows past M clamped)."""
     N, K = 320, 1152
@@ -282,7 +283,7 @@ def _linear_check(orc, x, packed, T, alpha, galpha, N, K, what):
     assert_y_close(gy.cpu().numpy(), y)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 100])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_linear_edges(orc, packed_cases, M, N, K):
     T, alpha, packed, galpha = packed_cases[(N, K)]
