@@ -107,7 +107,9 @@ constexpr bool quad_x(int MT, int MB) { return MT == 16 && MB >= 1; }
 // 5-bit Sherry code, 1 = the 2-bit baseline packing (its tile row is 8
 // dwords: lane group g takes dwords 2g and 2g+1, the same inputs
 // 32g..32g+31, through the same two transposes).  ST = register stages.
-template <int KW, int MT, int MB, bool FQ, int FMT, int ST>
+// FS = fused form: float4 loads per thread covering the tokens' rows
+// (>= M*K / (4 * 64 * KW); the launch picks the smallest power of two).
+template <int KW, int MT, int MB, bool FQ, int FMT, int ST, int FS = 1>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int splits, int kt_per_split) {
   static_assert(MB == 1 || (MT == 16 && !FQ), "several token blocks are whole blocks of 16");
   constexpr bool XQ = !FQ && quad_x(MT, MB);
@@ -148,8 +150,10 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
 
   // i-th k-tile of this wave (clamped: the prefetch past the end re-reads
   // the last tile, whose values are never used)
+  // (unconditional, so no branch merges the stage registers: a wave without
+  // k-tiles reads a valid tile of its row tile and never uses it)
   auto load = [&](int i, v4u& w, v4u& h, v4u (&x0)[MB], v4u (&x1)[MB]) {
-    const int kt = kt_begin + q + KW * min(i, nk - 1);
+    const int kt = min(kt_begin + q + KW * max(min(i, nk - 1), 0), KT - 1);
     const int ks = kt * TB, ka = kt * kTileK;
     w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
     if constexpr (FMT == 0) {
@@ -175,18 +179,29 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) acc[b][t] = v4i{0, 0, 0, 0};
 
+  // Fused form: the tokens' fp32 rows (M*K <= kFuseMaxMK floats) in one
+  // burst of loads, issued before the codes so that waiting for them does
+  // not wait for the code loads behind them.  Thread tid holds float4 F =
+  // tid + NT*j of the [M,K] block (zero past its end, through the buffer
+  // descriptor's range).
+  v4u xv[FS];
+  if constexpr (FQ) {
+    const __amdgpu_buffer_rsrc_t rxf = gemv_rsrc(a.xf, (size_t)M * (size_t)K * 4);
+#pragma unroll
+    for (int j = 0; j < FS; ++j) xv[j] = __builtin_amdgcn_raw_buffer_load_b128(rxf, 16 * (tid + NT * j), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // kStages register stages, filled kStages k-tiles ahead and used in turn.
   // The scheduling barriers keep every refill inside its own step, so a step
   // waits only for its own stage while the newer ones stay in flight.
   v4u cw[kStages];
   v4u ch[kStages];
   v4u xa[kStages][MB], xb[kStages][MB];
-  if (nk > 0) {
 #pragma unroll
-    for (int st = 0; st < kStages; ++st) {
-      load(st, cw[st], ch[st], xa[st], xb[st]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int st = 0; st < kStages; ++st) {
+    load(st, cw[st], ch[st], xa[st], xb[st]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (FMT == 0) {
     for (int i = tid; i < 1024; i += 64 * KW) dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
@@ -195,17 +210,22 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   }
   if constexpr (FQ) {
     // per-token scale over the whole row (every workgroup reads its tokens'
-    // rows; four loads in flight per thread per round)
+    // rows): the token of float4 F is the number of row ends at or below it
     const int K4 = K / 4;
+    auto token_of = [&](int F) { return (F >= K4) + (F >= 2 * K4) + (F >= 3 * K4); };
     float am[MT];
 #pragma unroll
+    for (int m = 0; m < MT; ++m) am[m] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < FS; ++j) {
+      const int m = token_of(tid + NT * j);
+      const float v = amax4(__builtin_bit_cast(float4, xv[j]));
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+        if (m == mm) am[mm] = fmaxf(am[mm], v);
+    }
+#pragma unroll
     for (int m = 0; m < MT; ++m) {
-      am[m] = 0.0f;
-      if (m < M) {
-        const float4* xr = reinterpret_cast<const float4*>(a.xf + (size_t)m * K);
-#pragma unroll 4
-        for (int e = tid; e < K4; e += NT) am[m] = fmaxf(am[m], amax4(xr[e]));
-      }
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) am[m] = fmaxf(am[m], __shfl_xor(am[m], off, 64));
       if (lane == 0) sred[q * MT + m] = am[m];
@@ -218,21 +238,22 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
       sred[KW * MT + tid] = v > 0.0f ? v / 127.0f : 1.0f;   // s = max|x| / 127; a zero row -> 1
     }
     __syncthreads();
-    // quantize this split's k-tiles of every token into LDS: q = clamp(rint(x / s))
-    const int n4 = span * (kTileK / 4);
+    // quantize this split's k-tiles of every token into LDS, from the
+    // registers: q = clamp(rint(x / s))
+    const int e0 = kt_begin * (kTileK / 4), e1 = e0 + span * (kTileK / 4);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < M) {
+    for (int j = 0; j < FS; ++j) {
+      const int F = tid + NT * j;
+      const int m = token_of(F);
+      const int e = F - m * K4;
+      if (m < M && e >= e0 && e < e1) {
         const float sm = sred[KW * MT + m];
-        const float4* xr = reinterpret_cast<const float4*>(a.xf + (size_t)m * K + (size_t)kt_begin * kTileK);
-        for (int e = tid; e < n4; e += NT) {
-          const float4 v = xr[e];
-          const uint32_t b0 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.x / sm), -127.0f), 127.0f);
-          const uint32_t b1 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.y / sm), -127.0f), 127.0f);
-          const uint32_t b2 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.z / sm), -127.0f), 127.0f);
-          const uint32_t b3 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.w / sm), -127.0f), 127.0f);
-          qs[(m * QS) / 4 + e] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-        }
+        const float4 v = __builtin_bit_cast(float4, xv[j]);
+        const uint32_t b0 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.x / sm), -127.0f), 127.0f);
+        const uint32_t b1 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.y / sm), -127.0f), 127.0f);
+        const uint32_t b2 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.z / sm), -127.0f), 127.0f);
+        const uint32_t b3 = (uint8_t)(int8_t)fminf(fmaxf(rintf(v.w / sm), -127.0f), 127.0f);
+        qs[(m * QS) / 4 + (e - e0)] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
       }
     }
   }
@@ -371,14 +392,32 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   }
 }
 
+template <int KW, int MT, int FS>
+hipError_t launch_fused_fs(const GemmPlan& p, const GemmArgs& a, hipStream_t stream, int need) {
+  if constexpr (FS < kFuseMaxMK / 4 / (64 * KW)) {
+    if (need > FS) return launch_fused_fs<KW, MT, 2 * FS>(p, a, stream, need);
+  }
+  if (need > FS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mfma_gemv_kernel<KW, MT, 1, true, 0, 4, FS>), dim3(p.grid), dim3(64 * KW), 0, stream, a,
+                     p.splits, p.kt_per_split);
+  return hipGetLastError();
+}
+
 template <int KW, bool FQ, int FMT>
 hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(p.grid), block(64 * KW);
-  if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1, 1, FQ, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2, 1, FQ, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4, 1, FQ, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-  else if constexpr (!FQ) {
-    if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+  if constexpr (FQ) {
+    // fused form: float4 loads per thread for the tokens' rows
+    const int need = (a.M * (a.K / 4) + 64 * KW - 1) / (64 * KW);
+    if (a.M <= 1) return launch_fused_fs<KW, 1, 1>(p, a, stream, need);
+    if (a.M <= 2) return launch_fused_fs<KW, 2, 1>(p, a, stream, need);
+    if (a.M <= 4) return launch_fused_fs<KW, 4, 1>(p, a, stream, need);
+    return hipErrorInvalidValue;
+  } else {
+    if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
     else if (a.M <= 16) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
     else if constexpr (FMT == 0 && KW <= 8) {   // 16 waves leave too few registers for two blocks
       if (a.M <= 32) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, 2, false, 0, 3>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
@@ -387,10 +426,8 @@ hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     } else {
       return hipErrorInvalidValue;
     }
-  } else {
-    return hipErrorInvalidValue;
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 template <bool FQ, int FMT>
