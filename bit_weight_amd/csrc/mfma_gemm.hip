@@ -320,7 +320,9 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
   // int32 sums into its parity's row-major LDS tile, then each thread adds
   // the two parities for 4 consecutive columns of one row and stores
   // y = ((float)acc * s_x[m]) * alpha[n] (or the int32 sum), 16 bytes per
-  // lane, so each store instruction writes whole 128-byte lines.  Lane
+  // lane, so each store instruction writes whole 128-byte lines, marked
+  // non-temporal (the output is not read again here: measured 7 % faster at
+  // M=512, N=14336, K=4096, where the 29 MB of fp32 output bound it).  Lane
   // (l16, g) of a 16 x 16 MFMA block holds column l16, rows 4g..4g+3.  The
   // scales are read once, before the first barrier.
   const bool want_y = a.y != nullptr;
@@ -355,9 +357,9 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
           const float sx = sxs[32 * qq + ml];
           const float4 v = make_float4(((float)sum.x * sx) * al4.x, ((float)sum.y * sx) * al4.y,
                                        ((float)sum.z * sx) * al4.z, ((float)sum.w * sx) * al4.w);
-          *reinterpret_cast<float4*>(a.y + (size_t)m * N + n) = v;
+          __builtin_nontemporal_store(__builtin_bit_cast(v4u, v), reinterpret_cast<v4u*>(a.y + (size_t)m * N + n));
         } else {
-          *reinterpret_cast<v4i*>(a.acc + (size_t)m * N + n) = sum;
+          __builtin_nontemporal_store(sum, reinterpret_cast<v4i*>(a.acc + (size_t)m * N + n));
         }
       }
     }
