@@ -50,6 +50,8 @@ def _load():
             "oracle_encode_block": [vp],
             "oracle_quantize": [vp, i64, i64, vp, vp],
             "oracle_pack": [vp, i64, i64, vp],
+            "oracle_packed_bytes": [i64, i64],
+            "oracle_packed2_bytes": [i64, i64],
             "oracle_unpack": [vp, i64, i64, vp],
             "oracle_pack2": [vp, i64, i64, vp],
             "oracle_unpack2": [vp, i64, i64, vp],
@@ -61,7 +63,7 @@ def _load():
         for name, args in sigs.items():
             fn = getattr(lib, name)
             fn.argtypes = args
-            fn.restype = ci
+            fn.restype = i64 if name.endswith("_bytes") else ci
         _lib = lib
     return _lib
 
@@ -106,11 +108,21 @@ def quantize(W: np.ndarray):
     return T, alpha
 
 
+def packed_bytes(N: int, K: int) -> int:
+    """Bytes of the 5-bit layout of an [N,K] matrix, padded to 64 x 128 tiles."""
+    return int(_load().oracle_packed_bytes(N, K))
+
+
+def packed2_bytes(N: int, K: int) -> int:
+    """Bytes of the 2-bit layout of an [N,K] matrix, padded to 64 x 128 tiles."""
+    return int(_load().oracle_packed2_bytes(N, K))
+
+
 def pack(T: np.ndarray) -> np.ndarray:
-    """Dense T -> packed bytes (N*K*5/32) in the tiled 5-bit layout."""
+    """Dense T -> packed bytes in the tiled 5-bit layout (padding: code 0)."""
     T = np.ascontiguousarray(T, dtype=np.int8)
     N, K = T.shape
-    out = np.empty(N * K * 5 // 32, np.uint8)
+    out = np.empty(packed_bytes(N, K), np.uint8)
     _check(_load().oracle_pack(_p(T), N, K, _p(out)), "pack")
     return out
 
@@ -118,17 +130,17 @@ def pack(T: np.ndarray) -> np.ndarray:
 def unpack(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     """Packed bytes -> dense T int8 [N,K]."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    assert packed.size == N * K * 5 // 32
+    assert packed.size == packed_bytes(N, K)
     T = np.empty((N, K), np.int8)
     _check(_load().oracle_unpack(_p(packed), N, K, _p(T)), "unpack")
     return T
 
 
 def pack2(T: np.ndarray) -> np.ndarray:
-    """Dense ternary T -> the 2-bit baseline format (N*K/4 bytes)."""
+    """Dense ternary T -> the 2-bit baseline format (padded like pack)."""
     T = np.ascontiguousarray(T, dtype=np.int8)
     N, K = T.shape
-    out = np.empty(N * K // 4, np.uint8)
+    out = np.empty(packed2_bytes(N, K), np.uint8)
     _check(_load().oracle_pack2(_p(T), N, K, _p(out)), "pack2")
     return out
 
@@ -136,7 +148,7 @@ def pack2(T: np.ndarray) -> np.ndarray:
 def unpack2(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     """2-bit baseline bytes -> dense T int8 [N,K]."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    assert packed.size == N * K // 4
+    assert packed.size == packed2_bytes(N, K)
     T = np.empty((N, K), np.int8)
     _check(_load().oracle_unpack2(_p(packed), N, K, _p(T)), "unpack2")
     return T

@@ -32,11 +32,14 @@
 //   * output: y = ((float)acc * s_x[m]) * alpha[n], float, round-to-nearest.
 //
 // Packed layout (the library's format; the oracle writes and reads it bit by
-// bit): W is [N,K] row-major, N % 64 == 0, K % 128 == 0.  Tiles of 64 rows x
-// 128 columns (32 blocks per row) are stored row-tile-major, column-tile
-// minor, 1280 bytes each.  A row's 32 codes form a 160-bit little-endian
-// string, code j at bits [5j, 5j+5).  Bits 0..127 of row r sit at tile byte
-// 16*r, bits 128..159 at tile byte 1024 + 4*r.  Total N*K*5/32 bytes.
+// bit): W is [N,K] row-major, K % 4 == 0.  The matrix is padded to Np =
+// N rounded up to 64 rows and Kp = K rounded up to 128 columns; tiles of 64
+// rows x 128 columns (32 blocks per row) are stored row-tile-major,
+// column-tile minor, 1280 bytes each.  A row's 32 codes form a 160-bit
+// little-endian string, code j at bits [5j, 5j+5).  Bits 0..127 of row r
+// sit at tile byte 16*r, bits 128..159 at tile byte 1024 + 4*r.  Blocks past
+// K and rows past N hold code 0 (they carry no weights; a product never
+// uses them).  Total Np*Kp*5/32 bytes.
 //
 // Build: g++ -std=c++17 -O2 -fno-fast-math -ffp-contract=off -shared -fPIC
 
@@ -94,10 +97,12 @@ int code_of_block(const int t[4]) {
   return 2 * p + s;
 }
 
+int64_t pad_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
 // Byte offset of the tile holding (row n, block b) and the row's slot in it.
 void tile_slot(int64_t n, int64_t b, int64_t K, int64_t* tile_base, int64_t* r,
                int* j) {
-  const int64_t KT = K / 128;
+  const int64_t KT = pad_to(K, 128) / 128;
   const int64_t rt = n / 64, kt = b / 32;
   *tile_base = (rt * KT + kt) * 1280;
   *r = n % 64;
@@ -166,10 +171,16 @@ int oracle_quantize(const float* W, int64_t N, int64_t K, int8_t* T,
   return 0;
 }
 
+// Bytes of the packed layout for an [N,K] matrix (padding included).
+int64_t oracle_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % 4 != 0) return -1;
+  return pad_to(N, 64) * pad_to(K, 128) * 5 / 32;
+}
+
 // Write T (exactly-3-nonzero ternary, [N,K]) in the packed layout.
 int oracle_pack(const int8_t* T, int64_t N, int64_t K, uint8_t* packed) {
-  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 128 != 0) return -1;
-  std::memset(packed, 0, (size_t)(N * K * 5 / 32));
+  if (N <= 0 || K <= 0 || K % 4 != 0) return -1;
+  std::memset(packed, 0, (size_t)oracle_packed_bytes(N, K));
   for (int64_t n = 0; n < N; ++n) {
     for (int64_t b = 0; b < K / 4; ++b) {
       int v[4];
@@ -192,9 +203,9 @@ int oracle_pack(const int8_t* T, int64_t N, int64_t K, uint8_t* packed) {
   return 0;
 }
 
-// Read the packed layout back into dense T.
+// Read the packed layout back into dense T (the [N,K] part).
 int oracle_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* T) {
-  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 128 != 0) return -1;
+  if (N <= 0 || K <= 0 || K % 4 != 0) return -1;
   for (int64_t n = 0; n < N; ++n) {
     for (int64_t b = 0; b < K / 4; ++b) {
       int64_t base, r;
@@ -222,10 +233,16 @@ int oracle_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* T) {
 // order as the 5-bit format.  A row's 128 weights form a 256-bit
 // little-endian string, weight j at bits [2j, 2j+2); bits 0..127 of tile
 // row r sit at tile byte 16*r, bits 128..255 at tile byte 1024 + 16*r.
+// Padded like the 5-bit format (to 64 rows and 128 columns; padding is 00).
+int64_t oracle_packed2_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % 4 != 0) return -1;
+  return pad_to(N, 64) * pad_to(K, 128) / 4;
+}
+
 int oracle_pack2(const int8_t* T, int64_t N, int64_t K, uint8_t* packed) {
-  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 128 != 0) return -1;
-  std::memset(packed, 0, (size_t)(N * K / 4));
-  const int64_t KT = K / 128;
+  if (N <= 0 || K <= 0 || K % 4 != 0) return -1;
+  std::memset(packed, 0, (size_t)oracle_packed2_bytes(N, K));
+  const int64_t KT = pad_to(K, 128) / 128;
   for (int64_t n = 0; n < N; ++n) {
     for (int64_t k = 0; k < K; ++k) {
       const int v = T[n * K + k];
@@ -245,8 +262,8 @@ int oracle_pack2(const int8_t* T, int64_t N, int64_t K, uint8_t* packed) {
 }
 
 int oracle_unpack2(const uint8_t* packed, int64_t N, int64_t K, int8_t* T) {
-  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 128 != 0) return -1;
-  const int64_t KT = K / 128;
+  if (N <= 0 || K <= 0 || K % 4 != 0) return -1;
+  const int64_t KT = pad_to(K, 128) / 128;
   for (int64_t n = 0; n < N; ++n) {
     for (int64_t k = 0; k < K; ++k) {
       const int64_t tile = ((n / 64) * KT + k / 128) * 2048;

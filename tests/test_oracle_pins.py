@@ -294,3 +294,28 @@ def test_pack2_roundtrip_any_ternary(orc):
     assert np.array_equal(orc.unpack2(orc.pack2(T3), 128, 256),
                           orc.unpack(orc.pack(T3), 128, 256))
     assert orc.pack2(T3).size * 5 == orc.pack(T3).size * 8   # 2 vs 1.25 bit per weight
+
+
+@pytest.mark.parametrize("N,K", [(70, 144), (1, 4), (64, 132), (100, 128), (65, 260)])
+def test_padded_layout_is_code_zero_padding(orc, N, K):
+    """A matrix whose N is not a multiple of 64 or whose K is not a multiple of
+    128 is stored as the padded matrix (N up to 64, K up to 128) whose extra
+    blocks are code 0, i.e. the block [0, +1, +1, +1]: its bytes equal those
+    of packing that padded matrix through the unpadded layout, and the
+    padding bytes are zero."""
+    rng = np.random.default_rng(N * 1000 + K)
+    T, _ = orc.quantize(rng.standard_normal((N, K)).astype(np.float32))
+    Np, Kp = -(-N // 64) * 64, -(-K // 128) * 128
+    assert orc.packed_bytes(N, K) == Np * Kp * 5 // 32
+    assert orc.packed2_bytes(N, K) == Np * Kp // 4
+    assert orc.encode_block(np.array([0, 1, 1, 1], np.int8)) == 0
+    full = np.tile(np.array([0, 1, 1, 1], np.int8), (Np, Kp // 4))
+    full[:N, :K] = T
+    P = orc.pack(T)
+    assert np.array_equal(P, orc.pack(full))
+    assert np.array_equal(orc.unpack(P, N, K), T)
+    # the same for the 2-bit format, whose padding is 00 (zero weights)
+    full2 = np.zeros((Np, Kp), np.int8)
+    full2[:N, :K] = T
+    assert np.array_equal(orc.pack2(T), orc.pack2(full2))
+    assert np.array_equal(orc.unpack2(orc.pack2(T), N, K), T)
