@@ -282,14 +282,18 @@ def linear(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, N: int, K
 
 
 def concat_packed(parts, Ns, K: int):
-    """Group several [N_i, K] packed matrices (e.g. q/k/v or gate/up, all
-    N_i % 64 == 0) into one [sum N_i, K] packed matrix.  The format keeps
-    each 64-row tile of every k-tile contiguous and orders tiles row group
-    first, so stacking weights along N stacks their packed bytes: the group
-    is plain concatenation, and one sherry_linear call on it computes every
-    member's output, sharing one activation quantization and one launch.
-    `parts` are (packed, alpha) pairs; returns (packed, alpha)."""
+    """Group several [N_i, K] packed matrices (e.g. q/k/v or gate/up; every
+    N_i but the last a multiple of 64) into one [sum N_i, K] packed matrix.
+    The format keeps each 64-row tile of every k-tile contiguous and orders
+    tiles row group first, so stacking weights along N stacks their packed
+    bytes: the group is plain concatenation, and one sherry_linear call on
+    it computes every member's output, sharing one activation quantization
+    and one launch.  (A part padded to whole row tiles would leave padding
+    rows inside the group, hence the rule.)  `parts` are (packed, alpha)
+    pairs; returns (packed, alpha)."""
     packs, alphas = [], []
+    if any(n % 64 for n in list(Ns)[:-1]):
+        raise RuntimeError("every part but the last needs N_i % 64 == 0 to stack")
     for (pk, al), n in zip(parts, Ns):
         if pk.numel() != packed_bytes(n, K) or al.numel() != n:
             raise RuntimeError("a part has the wrong size for its [N_i, K]")

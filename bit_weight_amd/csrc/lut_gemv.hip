@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
   __shared__ float fq_s[FQ ? 2 * MP : 1];               //   and the per-token scales
 
   const int M = a.M, N = a.N, K = a.K;
-  const int KT = K / kTileK, RT = N / kTileRows;
+  const int KT = k_tiles(K), RT = row_tiles(N);
   const int g = blockIdx.x / splits;
   const int s = blockIdx.x - g * splits;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -148,13 +148,14 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
         const int seg = rest / MP;
         const int k = kt_s * kTileK + 4 * seg;
         const int m0 = 2 * pair, m1 = 2 * pair + 1;
+        // segments past K (padding of a ragged last k-tile) get zero tables
         int x0 = 0, x1 = 0;
         if constexpr (FQ) {
-          if (m0 < M) x0 = quant_word(a.xf + (size_t)m0 * K + k, fq_s[m0]);
-          if (m1 < M) x1 = quant_word(a.xf + (size_t)m1 * K + k, fq_s[m1]);
+          if (m0 < M && k < K) x0 = quant_word(a.xf + (size_t)m0 * K + k, fq_s[m0]);
+          if (m1 < M && k < K) x1 = quant_word(a.xf + (size_t)m1 * K + k, fq_s[m1]);
         } else {
-          if (m0 < M) x0 = *reinterpret_cast<const int*>(a.x + (size_t)m0 * K + k);
-          if (m1 < M) x1 = *reinterpret_cast<const int*>(a.x + (size_t)m1 * K + k);
+          if (m0 < M && k < K) x0 = *reinterpret_cast<const int*>(a.x + (size_t)m0 * K + k);
+          if (m1 < M && k < K) x1 = *reinterpret_cast<const int*>(a.x + (size_t)m1 * K + k);
         }
         // the three kept positions in order: ja < jb < jc, none equal to z
         const int ja = z == 0 ? 1 : 0;
@@ -230,6 +231,7 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
 
   if (!active) return;
   const int n = rt * kTileRows + lane;
+  if (n >= N) return;                           // rows past N: padding, never stored
   const float al = a.y ? a.alpha[n] : 0.0f;
   // every token's atomic is issued before any result is used: one memory
   // round trip per lane whatever M is

@@ -113,7 +113,11 @@ template <bool kLive>
 __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kNT],
                                         const v4i (&b1)[kNT], const int8_t* as, int l16, int g,
                                         const uint32_t (&f0)[kNT], const uint32_t (&f1)[kNT],
-                                        v4i (&n0)[kNT], v4i (&n1)[kNT], const uint8_t* dec2) {
+                                        v4i (&n0)[kNT], v4i (&n1)[kNT], const uint8_t* dec2,
+                                        int nlim) {
+  // nlim: first input of this lane group in the next k-step, below K; the
+  // operands past K (padding of a ragged last k-tile) decode to zero
+  const v4i zero{0, 0, 0, 0};
   auto frag = [&](int u) {   // u = 8 s + row block
     return *reinterpret_cast<const v4i*>(as + a_off(16 * (u & 7) + l16, 2 * g + (u >> 3)));
   };
@@ -129,7 +133,10 @@ __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kN
       p0 = frag(u + 2);
       p1 = frag(u + 3);
     }
-    if (u >= kMT) n0[(u >> 1) & 3] = mg_decode4(f0[(u >> 1) & 3], dec2);
+    if (u >= kMT) {
+      const v4i d = mg_decode4(f0[(u >> 1) & 3], dec2);
+      n0[(u >> 1) & 3] = nlim > 0 ? d : zero;
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kLive) {
       const int i = u & 7;
@@ -145,7 +152,10 @@ __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kN
     a1 = p1;
   }
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) n1[t] = mg_decode4(f1[t], dec2);
+  for (int t = 0; t < kNT; ++t) {
+    const v4i d = mg_decode4(f1[t], dec2);
+    n1[t] = nlim > 16 ? d : zero;
+  }
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, size_t bytes) {
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
   __shared__ __attribute__((aligned(16))) uint2 dec2[1024];
   __shared__ float sxs[kBM];   // s_x of this tile's rows (epilogue)
 
-  const int M = a.M, N = a.N, K = a.K, KT = K / kTileK, RT = N / kTileRows;
+  const int M = a.M, N = a.N, K = a.K, KT = k_tiles(K), RT = row_tiles(N);
   // tile id -> (m tile, n tile): consecutive ids of one XCD share n tiles
   const int id = blockIdx.x;
   const int mt_count = (M + kBM - 1) / kBM;
@@ -227,10 +237,13 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
   auto copy_a = [&](int j, int b) {
     const int ka = ktile(j) * kBK;
     int8_t* dst = a_buf(b) + 32 * wave * kBK;
+    // (the k-step offset is added to the lane offset, not passed as the
+    // scalar offset, so the descriptor's range check covers a ragged last
+    // k-tile of the last row)
 #pragma unroll
     for (int jj = 0; jj < kACopies; ++jj)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(dst + 8 * jj * kBK), 16, a_v[jj], ka, 0, 0);
+          ra, (__attribute__((address_space(3))) void*)(dst + 8 * jj * kBK), 16, a_v[jj] + ka, 0, 0, 0);
   };
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
   // the 20-bit code groups of one register stage: lane (l16, g) of block t
@@ -266,10 +279,11 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
     split(wn, hn, f0, f1);
     load_codes(min(j + 3, KJ - 1), wn, hn);
     __builtin_amdgcn_sched_barrier(0);
+    const int nlim = K - ktile(j + 1) * kBK - 32 * g;
     if (2 * j + kh < KT)     // odd KT: the last pair has one k-tile
-      mg_mfma<true>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
+      mg_mfma<true>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2, nlim);
     else
-      mg_mfma<false>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
+      mg_mfma<false>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2, nlim);
   };
 
   // Two register stages of codes and two sets of B operands, ping-pong.
@@ -295,10 +309,13 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
   {
     uint32_t f0[kNT], f1[kNT];
     split(w0, h0, f0, f1);
+    const int lim0 = K - ktile(0) * kBK - 32 * g;
+    const v4i zero{0, 0, 0, 0};
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-      bA0[t] = mg_decode4(f0[t], d2);
-      bA1[t] = mg_decode4(f1[t], d2);
+      const v4i d0 = mg_decode4(f0[t], d2), d1 = mg_decode4(f1[t], d2);
+      bA0[t] = lim0 > 0 ? d0 : zero;
+      bA1[t] = lim0 > 16 ? d1 : zero;
     }
     load_codes(min(2, KJ - 1), w0, h0);
     __builtin_amdgcn_sched_barrier(0);

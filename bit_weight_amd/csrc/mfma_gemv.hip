@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   __shared__ __attribute__((aligned(16))) uint32_t qs[FQ ? MT * QS / 4 : 4];
   __shared__ float sred[FQ ? KW * MT + MT : 1];                          // partial maxima, scales
 
-  const int M = a.M, N = a.N, K = a.K, KT = K / kTileK;
+  const int M = a.M, N = a.N, K = a.K, KT = k_tiles(K);
   const int rt = blockIdx.x / splits;
   const int s = blockIdx.x - rt * splits;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -261,6 +261,10 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
 
   auto step = [&](int i, v4u& w, v4u& h, v4u (&x0)[MB], v4u (&x1)[MB]) {
+    // inputs of this lane group in this k-tile start at lim below K: past K
+    // (the padding of a ragged last k-tile) the decoded weights are zeroed
+    const int lim = K - (kt_begin + q + KW * i) * kTileK - 32 * g;
+    const v4i zero{0, 0, 0, 0};
     uint32_t lo[kBlk], hi[kBlk];
     uint32_t f0[kBlk], f1[kBlk];
     if constexpr (FMT == 0) {
@@ -305,13 +309,15 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
-      const v4i bw = FMT == 0 ? decode4(f0[t], d2) : decode16(f0[t], tbl2);
+      const v4i bd = FMT == 0 ? decode4(f0[t], d2) : decode16(f0[t], tbl2);
+      const v4i bw = lim > 0 ? bd : zero;
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[b], bw, acc[b][t], 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
-      const v4i bw = FMT == 0 ? decode4(f1[t], d2) : decode16(f1[t], tbl2);
+      const v4i bd = FMT == 0 ? decode4(f1[t], d2) : decode16(f1[t], tbl2);
+      const v4i bw = lim > 16 ? bd : zero;
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[b], bw, acc[b][t], 0, 0, 0);
     }
@@ -333,7 +339,9 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   // the padded count add 0 to the cell of token M-1, which changes nothing.
   constexpr int TPW = MT >= KW ? MT / KW : 1;        // tokens per wave and block
   const int n = rt * kTileRows + lane;
-  const float al = a.y ? a.alpha[n] : 0.0f;
+  const bool n_ok = n < N;                            // rows past N: padding, never stored
+  const int nc = min(n, N - 1);                       // a valid column for their no-op atomics
+  const float al = a.y && n_ok ? a.alpha[n] : 0.0f;
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
     if (b > 0) __syncthreads();   // the previous block's sums are read
@@ -363,8 +371,8 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
       for (int i = 0; i < TPW; ++i) {
         const int m = 16 * b + q * TPW + i;
         const unsigned long long inc =
-            m < M ? (1ull << 32) + (unsigned long long)(long long)total[i] : 0ull;
-        now[i] = __hip_atomic_fetch_add(cells + (size_t)min(m, M - 1) * N + n, inc, __ATOMIC_RELAXED,
+            m < M && n_ok ? (1ull << 32) + (unsigned long long)(long long)total[i] : 0ull;
+        now[i] = __hip_atomic_fetch_add(cells + (size_t)min(m, M - 1) * N + nc, inc, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
@@ -374,14 +382,14 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
         total[i] = (int)(uint32_t)now[i];
         // the high word minus the borrow of a negative low word = arrivals
         last[i] = (((long long)now[i] - (long long)total[i]) >> 32) == (long long)splits;
-        if (m < M && last[i])
+        if (m < M && n_ok && last[i])
           __hip_atomic_store(cells + (size_t)m * N + n, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int m = 16 * b + q * TPW + i;
-      if (m >= M || !last[i]) continue;
+      if (m >= M || !n_ok || !last[i]) continue;
       if (a.y) {
         const float tv = (float)total[i] * (FQ ? sred[KW * MT + m] : a.s_x[m]);
         a.y[(size_t)m * N + n] = tv * al;

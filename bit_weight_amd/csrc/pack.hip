@@ -33,19 +33,21 @@ __device__ __forceinline__ uint32_t encode_block(float w0, float w1, float w2, f
 }
 
 // One wave per format tile: lane r encodes the 32 blocks of tile row r and
-// writes its 16 + 4 bytes (both stores coalesced across the wave).
+// writes its 16 + 4 bytes (both stores coalesced across the wave).  Rows
+// past N and blocks past K (padding) get code 0 and read nothing.
 __global__ __launch_bounds__(64) void pack_codes_kernel(const float* __restrict__ W,
                                                         uint8_t* __restrict__ packed,
                                                         int N, int K) {
-  const int KT = K / kTileK;
+  const int KT = k_tiles(K);
   const int rt = blockIdx.x / KT, kt = blockIdx.x % KT;
   const int lane = threadIdx.x;
   const int n = rt * kTileRows + lane;
-  if (n >= N) return;
-  const float4* src = reinterpret_cast<const float4*>(W + (size_t)n * K + (size_t)kt * kTileK);
+  const int nb = n < N ? min(32, (K - kt * kTileK) / 4) : 0;   // real blocks of this row
+  const float4* src = reinterpret_cast<const float4*>(W + (size_t)min(n, N - 1) * K + (size_t)kt * kTileK);
   uint32_t w[5] = {0, 0, 0, 0, 0};
 #pragma unroll
   for (int b = 0; b < 32; ++b) {
+    if (b >= nb) continue;
     const float4 v = src[b];
     const uint32_t c = encode_block(v.x, v.y, v.z, v.w);
     const int bit = 5 * b, d = bit >> 5, sh = bit & 31;
@@ -63,15 +65,16 @@ __global__ __launch_bounds__(64) void pack_codes_kernel(const float* __restrict_
 __global__ __launch_bounds__(64) void pack2_codes_kernel(const float* __restrict__ W,
                                                          uint8_t* __restrict__ packed,
                                                          int N, int K) {
-  const int KT = K / kTileK;
+  const int KT = k_tiles(K);
   const int rt = blockIdx.x / KT, kt = blockIdx.x % KT;
   const int lane = threadIdx.x;
   const int n = rt * kTileRows + lane;
-  if (n >= N) return;
-  const float4* src = reinterpret_cast<const float4*>(W + (size_t)n * K + (size_t)kt * kTileK);
+  const int nb = n < N ? min(32, (K - kt * kTileK) / 4) : 0;   // real blocks (padding: 00)
+  const float4* src = reinterpret_cast<const float4*>(W + (size_t)min(n, N - 1) * K + (size_t)kt * kTileK);
   uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int b = 0; b < 32; ++b) {
+    if (b >= nb) continue;
     const float4 v = src[b];
     // the block's values from its 5-bit code, then 2 bits per weight
     const uint32_t cw = code_word(encode_block(v.x, v.y, v.z, v.w));
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
 
 hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, float* alpha,
                                 hipStream_t stream) {
-  const int tiles = (N / kTileRows) * (K / kTileK);
+  const int tiles = row_tiles(N) * k_tiles(K);
   hipLaunchKernelGGL(pack_codes_kernel, dim3(tiles), dim3(64), 0, stream, W, packed, N, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -191,7 +194,7 @@ hipError_t launch_quantize_pack(const float* W, int N, int K, uint8_t* packed, f
 
 hipError_t launch_quantize_pack2(const float* W, int N, int K, uint8_t* packed, float* alpha,
                                  hipStream_t stream) {
-  const int tiles = (N / kTileRows) * (K / kTileK);
+  const int tiles = row_tiles(N) * k_tiles(K);
   hipLaunchKernelGGL(pack2_codes_kernel, dim3(tiles), dim3(64), 0, stream, W, packed, N, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

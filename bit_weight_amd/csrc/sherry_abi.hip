@@ -37,9 +37,13 @@ sherry_status check_device() {
   return g_dev_ok[dev] == 1 ? SHERRY_OK : SHERRY_ERR_DEVICE;
 }
 
+// K % 16: whole 4-weight blocks, and int8 activation rows 16-byte aligned
+// for the kernels' 16-byte loads; N % 4: the prefill epilogue's 16-byte
+// stores stay inside a row.  Other multiples of the 64 x 128 tiles are
+// padding of the packed format.
 bool shape_ok(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && N >= 1 && K >= 1 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim &&
-         K % kTileK == 0 && N % kTileRows == 0;
+         K % 16 == 0 && N % 4 == 0;
 }
 
 }  // namespace
@@ -54,7 +58,7 @@ std::atomic<int> g_ovr_path{-1}, g_ovr_rw{0}, g_ovr_ch{0}, g_ovr_splits{0};
 // each wave has at most ~3 k-tiles (measured on MI355X at the LLaMA shapes).
 GemmPlan plan_mfma_gemv(int M, int N, int K) {
   GemmPlan p{};
-  const int KT = K / kTileK, RT = N / kTileRows;
+  const int KT = k_tiles(K), RT = row_tiles(N);
   const int ovr_kw = g_ovr_rw.load();
   int kw = ovr_kw == 4 || ovr_kw == 8 || ovr_kw == 16 ? ovr_kw : (RT >= 128 ? 8 : 4);
   if (M > 16 && kw > 8) kw = 8;   // several token blocks: at most 8 waves
@@ -125,7 +129,7 @@ GemmPlan plan_prefill(int M, int N, int K) {
   p.grid = mfma_gemm_grid(M, N);
   p.block = mfma_gemm_threads();
   p.splits = 1;
-  p.kt_per_split = K / kTileK;
+  p.kt_per_split = k_tiles(K);
   p.lds_bytes = mfma_gemm_lds_bytes();
   p.ws_bytes = 0;
   return p;
@@ -151,8 +155,8 @@ GemmPlan plan_gemm(int M, int N, int K) {
   if (path == 1) return plan_prefill(M, N, K);
   if (path == 2) return plan_mfma_gemv(M, N, K);
   const int MP = (M + 1) / 2;
-  const int KT = K / kTileK;
-  const int RT = N / kTileRows;
+  const int KT = k_tiles(K);
+  const int RT = row_tiles(N);
   int ch_max = 1;                       // one stage of tables stays <= 32 KB
   while (ch_max < 8 && (ch_max * 2) * MP <= 8) ch_max *= 2;
 
@@ -243,7 +247,7 @@ const char* sherry_status_string(int status) {
   switch (status) {
     case SHERRY_OK: return "SHERRY_OK";
     case SHERRY_ERR_NULL: return "SHERRY_ERR_NULL: a required pointer is NULL";
-    case SHERRY_ERR_SHAPE: return "SHERRY_ERR_SHAPE: need 1<=M,N,K<=2^20, K%128==0, N%64==0";
+    case SHERRY_ERR_SHAPE: return "SHERRY_ERR_SHAPE: need 1<=M,N,K<=2^20, K%16==0, N%4==0";
     case SHERRY_ERR_ALIGN: return "SHERRY_ERR_ALIGN: pointer alignment requirement not met";
     case SHERRY_ERR_WORKSPACE: return "SHERRY_ERR_WORKSPACE: workspace missing or too small";
     case SHERRY_ERR_HIP: return "SHERRY_ERR_HIP: a HIP call or kernel launch failed";
@@ -254,7 +258,7 @@ const char* sherry_status_string(int status) {
 
 size_t sherry_packed_bytes(int64_t N, int64_t K) {
   if (!shape_ok(1, N, K)) return 0;
-  return (size_t)N * (size_t)K * 5 / 32;
+  return (size_t)row_tiles((int)N) * (size_t)k_tiles((int)K) * kTileBytes;
 }
 
 size_t sherry_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -322,7 +326,7 @@ sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,
 
 size_t sherry_packed2_bytes(int64_t N, int64_t K) {
   if (!shape_ok(1, N, K)) return 0;
-  return (size_t)N * (size_t)K / 4;
+  return (size_t)row_tiles((int)N) * (size_t)k_tiles((int)K) * kTile2Bytes;
 }
 
 sherry_status sherry_quantize_pack2(const float* W, int64_t N, int64_t K, void* packed, float* alpha,

@@ -15,6 +15,11 @@ constexpr int kTileK = 128;       // weights per row per tile (32 blocks)
 constexpr int kTileBytes = 1280;  // 64 rows * 32 codes * 5 bits / 8
 constexpr int kTileHiOff = 1024;  // byte offset of the 4-byte code parts
 
+// Tiles of an [N,K] matrix: padded to whole 64-row x 128-column tiles whose
+// extra blocks hold code 0 and are never used by a product.
+__host__ __device__ constexpr int row_tiles(int N) { return (N + kTileRows - 1) / kTileRows; }
+__host__ __device__ constexpr int k_tiles(int K) { return (K + kTileK - 1) / kTileK; }
+
 // Value (-1, 0 or +1) at position j of the block whose code is c.  The
 // pattern index p = c >> 1 names the zero position z = p >> 2 and whether
 // the 2nd / 3rd nonzero (in position order) flips sign relative to the 1st;

@@ -28,7 +28,9 @@
  *     enqueues nothing and returns a negative status.  A failed launch
  *     returns SHERRY_ERR_HIP.  A fault inside a kernel is reported by the
  *     caller's next synchronizing HIP call, not by this library.
- *   - Shapes supported: K % 128 == 0, N % 64 == 0, 1 <= M,N,K <= 2^20.
+ *   - Shapes supported: K % 16 == 0, N % 4 == 0, 1 <= M,N,K <= 2^20
+ *     (whole 4-weight blocks, 16-byte aligned int8 activation rows and
+ *     whole 16-byte output stores).
  *   - Code 5-bit layout ("packed"): code c = 2*p + s per block; p = 4*z +
  *     2*r1 + r2 where z is the zero position and r1 (r2) says the 2nd (3rd)
  *     nonzero's sign differs from the 1st's; s = 1 iff the 1st nonzero is -1.
@@ -36,7 +38,10 @@
  *     row-tile-major and column-tile-minor.  A row's 32 codes in a tile form
  *     a 160-bit little-endian string with code j at bits [5j, 5j+5); bits
  *     0..127 of tile row r sit at tile byte 16*r and bits 128..159 at tile
- *     byte 1024 + 4*r.  Total sherry_packed_bytes(N,K) = N*K*5/32 bytes.
+ *     byte 1024 + 4*r.  The matrix is padded to whole tiles (N up to a
+ *     multiple of 64, K up to a multiple of 128); padding blocks hold code 0
+ *     and no product uses them.  Total sherry_packed_bytes(N,K) =
+ *     ceil(N/64) * ceil(K/128) * 1280 bytes (N*K*5/32 when no padding).
  */
 #ifndef SHERRY_H
 #define SHERRY_H
@@ -162,7 +167,8 @@ sherry_status sherry_linear(const float* x, const void* packed, const float* alp
  * row's 256-bit little-endian string, bits 0..127 at tile byte 16*r and bits
  * 128..255 at tile byte 1024 + 16*r.  Same shape rules as the 5-bit format. */
 
-/* N*K/4; host-only, pure; 0 for an unsupported shape. */
+/* ceil(N/64) * ceil(K/128) * 2048 (N*K/4 when no padding; padding is 00);
+ * host-only, pure; 0 for an unsupported shape. */
 size_t sherry_packed2_bytes(int64_t N, int64_t K);
 
 /* As sherry_quantize_pack, output in the 2-bit format (packed: 16-byte

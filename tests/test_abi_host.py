@@ -44,8 +44,12 @@ def test_packed_bytes():
     assert bw.packed_bytes(14336, 4096) == 9_175_040
     assert bw.packed_bytes(4096, 11008) == 7_045_120
     assert bw.packed_bytes(256, 256) == 10_240
-    assert bw.packed_bytes(64, 100) == 0          # K % 128 != 0
-    assert bw.packed_bytes(65, 128) == 0          # N % 64 != 0
+    assert bw.packed_bytes(64, 100) == 0          # K % 16 != 0
+    assert bw.packed_bytes(66, 128) == 0          # N % 4 != 0
+    # ragged shapes are padded to whole 64 x 128 tiles of 1280 bytes
+    assert bw.packed_bytes(68, 144) == 2 * 2 * 1280
+    assert bw.packed_bytes(4, 16) == 1280
+    assert bw.lib().sherry_packed2_bytes(68, 144) == 2 * 2 * 2048
 
 
 def test_plan_dispatch_rule():
@@ -119,7 +123,7 @@ def test_gemm_null_pointers():
 
 
 @pytest.mark.parametrize("M,N,K", [(0, 64, 128), (1, 0, 128), (1, 64, 0), (1, 64, 100),
-                                   (1, 64, 132), (1, 65, 128), (1, 96, 128), (-1, 64, 128),
+                                   (1, 64, 132), (1, 65, 128), (1, 98, 128), (-1, 64, 128),
                                    (1, 64, (1 << 20) + 128), (1 << 21, 64, 128)])
 def test_gemm_bad_shapes(M, N, K):
     assert _gemm(M=M, N=N, K=K) == SHAPE
@@ -184,7 +188,7 @@ def test_linear_scratch_and_validation():
     for k in ("x", "p", "al", "y"):
         assert L.sherry_linear(*args(**{k: None})) == NULL, k
     assert L.sherry_linear(*args(K=100)) == SHAPE
-    assert L.sherry_linear(*args(N=96)) == SHAPE
+    assert L.sherry_linear(*args(N=98)) == SHAPE
     assert L.sherry_linear(*args(x=FAKE + 4)) == ALIGN
     assert L.sherry_linear(*args(p=FAKE + 8)) == ALIGN
     M, N, K = 16, 4096, 4096

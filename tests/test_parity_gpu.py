@@ -45,7 +45,9 @@ def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray):
 
 # ---------------------------------------------------------------- packer
 @pytest.mark.parametrize("N,K,std,spikes", [(64, 128, 0.02, False), (256, 256, 0.02, False),
-                                            (192, 384, 0.1, True), (320, 1152, 0.02, False)])
+                                            (192, 384, 0.1, True), (320, 1152, 0.02, False),
+                                            (68, 144, 0.02, False), (4, 16, 0.1, True),
+                                            (196, 1040, 0.1, True)])
 def test_pack_parity(orc, N, K, std, spikes):
     _say(f"pack N={N} K={K}")
     W = synth.weights(N, K, std, spikes, seed=100 + N + K)
@@ -416,3 +418,81 @@ def test_gemm2_workloads(orc, name):
     torch.cuda.synchronize()
     assert np.array_equal(p2.cpu().numpy(), orc.pack2(T))
     assert_y_close(gy.cpu().numpy(), y)
+
+
+# ------------------------------------------- ragged shapes (padded tiles)
+RAGGED = [(68, 144), (4, 16), (196, 1040), (452, 272)]
+
+
+@pytest.fixture(scope="module")
+def ragged_cases(orc):
+    out = {}
+    for (N, K) in RAGGED:
+        W = synth.weights(N, K, 0.02, False, seed=8100 + N + K)
+        T, alpha = orc.quantize(W.numpy())
+        packed, galpha = gpu_pack(W)
+        assert np.array_equal(packed.cpu().numpy(), orc.pack(T))
+        out[(N, K)] = (T, alpha, packed, galpha)
+    return out
+
+
+RAGGED_PLANS = [(None, 0, 0), ("decode_mfma_gemv", 4, 3), ("decode_mfma_gemv", 16, 1),
+                ("decode_mfma_gemv", 8, 2), ("lut_gemv", 0, 0), ("lut_gemv", 1, 3),
+                ("decode_mfma", 0, 0)]
+
+
+@pytest.mark.parametrize("path,rw,splits,M", [
+    (p, rw, sp, M) for (p, rw, sp) in RAGGED_PLANS for M in (1, 3, 9, 16, 40, 100, 129)
+    if not (p == "lut_gemv" and M > 16)])        # the lookup-table path takes M <= 16
+@pytest.mark.parametrize("N,K", RAGGED)
+def test_gemm_ragged(orc, ragged_cases, path, rw, splits, M, N, K):
+    """N not a multiple of 64 and K not a multiple of 128, on every path: the
+    padding rows are not stored and the padding blocks add nothing."""
+    T, alpha, packed, galpha = ragged_cases[(N, K)]
+    q = synth.int8_uniform(M, K, seed=8300 + M + K)
+    s_x = (torch.rand(M, generator=torch.Generator().manual_seed(M + 11)) * 0.05 + 0.001).float()
+    acc, y = orc.gemm(q.numpy(), s_x.numpy(), T, alpha)
+    try:
+        bw.plan_override(path, rw, 0, splits)
+        _say(f"ragged gemm {path} rw={rw} splits={splits} M={M} N={N} K={K}: {bw.plan(M, N, K)}")
+        gacc = bw.gemm_i32(q.cuda(), packed, N, K)
+        gy = bw.gemm(q.cuda(), s_x.cuda(), packed, galpha, N, K)
+        torch.cuda.synchronize()
+    finally:
+        bw.plan_override()
+    assert np.array_equal(gacc.cpu().numpy(), acc)
+    assert_y_close(gy.cpu().numpy(), y)
+
+
+@pytest.mark.parametrize("path", [None, "lut_gemv", "decode_mfma"])
+@pytest.mark.parametrize("M", [1, 2, 4, 7])
+@pytest.mark.parametrize("N,K", RAGGED)
+def test_linear_ragged(orc, ragged_cases, path, M, N, K):
+    T, alpha, packed, galpha = ragged_cases[(N, K)]
+    x = synth.activations(M, K, seed=8500 + M + K, outlier_channels=True)
+    try:
+        bw.plan_override(path)
+        _say(f"ragged linear {path} M={M} N={N} K={K}")
+        _linear_check(orc, x, packed, T, alpha, galpha, N, K, f"{path} M={M}")
+    finally:
+        bw.plan_override()
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("N,K", RAGGED)
+def test_gemm2_ragged(orc, M, N, K):
+    """The 2-bit format padded the same way; its product equals the 5-bit one."""
+    W = synth.weights(N, K, 0.02, False, seed=8700 + N + K)
+    T, alpha = orc.quantize(W.numpy())
+    p5, a5 = gpu_pack(W)
+    p2, a2 = bw.quantize_pack2(W.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(p2.cpu().numpy(), orc.pack2(T))
+    q = synth.int8_uniform(M, K, seed=8800 + M)
+    s_x = (torch.rand(M, generator=torch.Generator().manual_seed(M + 5)) * 0.05 + 0.001).float()
+    acc, y = orc.gemm(q.numpy(), s_x.numpy(), T, alpha)
+    gy2 = bw.gemm2(q.cuda(), s_x.cuda(), p2, a2, N, K)
+    gy5 = bw.gemm(q.cuda(), s_x.cuda(), p5, a5, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(gy2.cpu().numpy().view(np.uint32), gy5.cpu().numpy().view(np.uint32))
+    assert_y_close(gy2.cpu().numpy(), y)
