@@ -113,11 +113,7 @@ template <bool kLive>
 __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kNT],
                                         const v4i (&b1)[kNT], const int8_t* as, int l16, int g,
                                         const uint32_t (&f0)[kNT], const uint32_t (&f1)[kNT],
-                                        v4i (&n0)[kNT], v4i (&n1)[kNT], const uint8_t* dec2,
-                                        int nlim) {
-  // nlim: first input of this lane group in the next k-step, below K; the
-  // operands past K (padding of a ragged last k-tile) decode to zero
-  const v4i zero{0, 0, 0, 0};
+                                        v4i (&n0)[kNT], v4i (&n1)[kNT], const uint8_t* dec2) {
   auto frag = [&](int u) {   // u = 8 s + row block
     return *reinterpret_cast<const v4i*>(as + a_off(16 * (u & 7) + l16, 2 * g + (u >> 3)));
   };
@@ -133,10 +129,7 @@ __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kN
       p0 = frag(u + 2);
       p1 = frag(u + 3);
     }
-    if (u >= kMT) {
-      const v4i d = mg_decode4(f0[(u >> 1) & 3], dec2);
-      n0[(u >> 1) & 3] = nlim > 0 ? d : zero;
-    }
+    if (u >= kMT) n0[(u >> 1) & 3] = mg_decode4(f0[(u >> 1) & 3], dec2);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kLive) {
       const int i = u & 7;
@@ -152,10 +145,7 @@ __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kN
     a1 = p1;
   }
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    const v4i d = mg_decode4(f1[t], dec2);
-    n1[t] = nlim > 16 ? d : zero;
-  }
+  for (int t = 0; t < kNT; ++t) n1[t] = mg_decode4(f1[t], dec2);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, size_t bytes) {
@@ -215,6 +205,13 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     a_v[jj] = min(row, M - 1 - m0) * K + c * 16;
   }
+  // first input of a copy's chunk in its k-step: the swizzle (row >> 1) & 7
+  // of row 32 wave + 8 jj + (lane >> 3) is 4 (jj & 1) + (lane >> 4)
+  int a_k[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) a_k[p] = 16 * ((lane & 7) ^ (4 * p + (lane >> 4)));
+  // an offset the descriptor's range check rejects (the copy writes zeros)
+  const int a_oob = (size_t)(M - m0) * (size_t)K > 0x7FFFFFFFull ? 0x7FFFFFFF : (M - m0) * K;
   auto a_buf = [&](int b) { return reinterpret_cast<int8_t*>(lds) + (b * 2 + kh) * kAStage; };
 
   v4i acc[kMT][kNT];
@@ -238,12 +235,14 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
     const int ka = ktile(j) * kBK;
     int8_t* dst = a_buf(b) + 32 * wave * kBK;
     // (the k-step offset is added to the lane offset, not passed as the
-    // scalar offset, so the descriptor's range check covers a ragged last
-    // k-tile of the last row)
+    // scalar offset, so the descriptor's range check sees the whole offset;
+    // chunks past K, in a ragged last k-tile whose codes are padding, take
+    // an out-of-range offset and land as zeros)
 #pragma unroll
     for (int jj = 0; jj < kACopies; ++jj)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(dst + 8 * jj * kBK), 16, a_v[jj] + ka, 0, 0, 0);
+          ra, (__attribute__((address_space(3))) void*)(dst + 8 * jj * kBK), 16,
+          ka + a_k[jj & 1] < K ? a_v[jj] + ka : a_oob, 0, 0, 0);
   };
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
   // the 20-bit code groups of one register stage: lane (l16, g) of block t
@@ -279,11 +278,10 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
     split(wn, hn, f0, f1);
     load_codes(min(j + 3, KJ - 1), wn, hn);
     __builtin_amdgcn_sched_barrier(0);
-    const int nlim = K - ktile(j + 1) * kBK - 32 * g;
     if (2 * j + kh < KT)     // odd KT: the last pair has one k-tile
-      mg_mfma<true>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2, nlim);
+      mg_mfma<true>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
     else
-      mg_mfma<false>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2, nlim);
+      mg_mfma<false>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
   };
 
   // Two register stages of codes and two sets of B operands, ping-pong.
@@ -309,13 +307,10 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
   {
     uint32_t f0[kNT], f1[kNT];
     split(w0, h0, f0, f1);
-    const int lim0 = K - ktile(0) * kBK - 32 * g;
-    const v4i zero{0, 0, 0, 0};
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-      const v4i d0 = mg_decode4(f0[t], d2), d1 = mg_decode4(f1[t], d2);
-      bA0[t] = lim0 > 0 ? d0 : zero;
-      bA1[t] = lim0 > 16 ? d1 : zero;
+      bA0[t] = mg_decode4(f0[t], d2);
+      bA1[t] = mg_decode4(f1[t], d2);
     }
     load_codes(min(2, KJ - 1), w0, h0);
     __builtin_amdgcn_sched_barrier(0);

@@ -141,6 +141,11 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   const size_t tb = (size_t)rt * KT * TB;
   const __amdgpu_buffer_rsrc_t rc = gemv_rsrc(a.packed + tb, (size_t)KT * TB);
   const __amdgpu_buffer_rsrc_t rx = gemv_rsrc(a.x, (size_t)M * (size_t)K);
+  // an offset the descriptor's range check rejects (the load returns zeros)
+  const int x_oob = (size_t)M * (size_t)K > 0x7FFFFFFFull ? 0x7FFFFFFF : M * K;
+  // first input of the 16-byte chunks this lane loads (lane group g, or in
+  // the four-lanes-per-row load layout g' = lane & 3)
+  const int x_k = 32 * (XQ ? (lane & 3) : g);
   // lane offset of the activations (>= M*K for the padding tokens; the
   // k-tile offset is added to it, not passed as the scalar offset, so the
   // descriptor's range check sees the whole offset)
@@ -161,11 +166,14 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
     } else {
       h = __builtin_amdgcn_raw_buffer_load_b128(rc, kTile2HiOff + 16 * lane, ks, 0);
     }
+    // chunks past K (a ragged last k-tile, whose codes are padding) load as
+    // zeros: the offset is chosen before the load, so nothing waits for it
+    const bool in0 = ka + x_k < K, in1 = ka + x_k + 16 < K;
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
       if constexpr (!FQ) {
-        x0[b] = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + 16 * b * K + ka, 0, 0);
-        x1[b] = __builtin_amdgcn_raw_buffer_load_b128(rx, x_v + 16 * b * K + ka + 16, 0, 0);
+        x0[b] = __builtin_amdgcn_raw_buffer_load_b128(rx, in0 ? x_v + 16 * b * K + ka : x_oob, 0, 0);
+        x1[b] = __builtin_amdgcn_raw_buffer_load_b128(rx, in1 ? x_v + 16 * b * K + ka + 16 : x_oob, 0, 0);
       } else {
         x0[b] = v4u{0u, 0u, 0u, 0u};
         x1[b] = v4u{0u, 0u, 0u, 0u};
@@ -256,15 +264,16 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
         qs[(m * QS) / 4 + (e - e0)] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
       }
     }
+    // a ragged last k-tile: inputs past K read as zero
+    for (int e = max(e0, K4) + tid; e < e1; e += NT)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < M) qs[(m * QS) / 4 + (e - e0)] = 0u;
   }
   lds_barrier();
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
 
   auto step = [&](int i, v4u& w, v4u& h, v4u (&x0)[MB], v4u (&x1)[MB]) {
-    // inputs of this lane group in this k-tile start at lim below K: past K
-    // (the padding of a ragged last k-tile) the decoded weights are zeroed
-    const int lim = K - (kt_begin + q + KW * i) * kTileK - 32 * g;
-    const v4i zero{0, 0, 0, 0};
     uint32_t lo[kBlk], hi[kBlk];
     uint32_t f0[kBlk], f1[kBlk];
     if constexpr (FMT == 0) {
@@ -309,15 +318,13 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
-      const v4i bd = FMT == 0 ? decode4(f0[t], d2) : decode16(f0[t], tbl2);
-      const v4i bw = lim > 0 ? bd : zero;
+      const v4i bw = FMT == 0 ? decode4(f0[t], d2) : decode16(f0[t], tbl2);
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[b], bw, acc[b][t], 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
-      const v4i bd = FMT == 0 ? decode4(f1[t], d2) : decode16(f1[t], tbl2);
-      const v4i bw = lim > 16 ? bd : zero;
+      const v4i bw = FMT == 0 ? decode4(f1[t], d2) : decode16(f1[t], tbl2);
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[b], bw, acc[b][t], 0, 0, 0);
     }
