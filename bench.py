@@ -346,16 +346,18 @@ def main():
     gemm_ms, _ = graph_time(torch, lambda i: st.gemm(bw, i), n_k, reps=3)
     act_ms, _ = graph_time(torch, lambda i: bw.quantize_act(st.x), n_k, reps=3)
     plan = bw.plan(w.M, w.N, w.K)
-    kern = PATH_KERNEL[plan["path"]]
-    fused = bw.linear_scratch_bytes(w.M, w.N, w.K) == 0
+    lplan = bw.linear_plan(w.M, w.N, w.K)
+    fused = lplan["fused"]
     if fused:
-        # the step is one kernel (quantization fused into the product): its
-        # duration is the timed region's per-step time, and its algorithmic
-        # bytes read the fp32 activations
+        # the step is one kernel (quantization fused into the product, on
+        # sherry_linear's own plan): its duration is the timed region's
+        # per-step time, and its algorithmic bytes read the fp32 activations
+        kern = PATH_KERNEL[lplan["path"]]
         alg = algorithmic_bytes(w, fp32_x=True)
         kern_ms = step_ms
-        traffic = traffic_from_profile(kern + "_fused", name, plan)
+        traffic = traffic_from_profile(kern + "_fused", name, lplan)
     else:
+        kern = PATH_KERNEL[plan["path"]]
         alg = algorithmic_bytes(w)
         kern_ms = gemm_ms
         traffic = traffic_from_profile(kern, name, plan)
@@ -379,8 +381,9 @@ def main():
                    "M": w.M, "K": w.K, "N": w.N, "weights": f"Normal(0,{w.w_std})",
                    "rotating_copies": st.R,
                    "step": "sherry_linear (per-token int8 quantization + product)",
-                   "linear_fused": bw.linear_scratch_bytes(w.M, w.N, w.K) == 0,
-                   "plan": bw.plan(w.M, w.N, w.K), "parallelism": "none (1 GPU)"},
+                   "linear_fused": fused,
+                   "plan": {k: v for k, v in lplan.items() if k != "fused"},
+                   "gemm_plan": plan, "parallelism": "none (1 GPU)"},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

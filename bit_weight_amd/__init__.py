@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
                 "sherry_workspace_bytes": ([i64, i64, i64], sz),
                 "sherry_gemm_plan": ([i64, i64, i64, ip, ip, ip, ip, ip], ci),
                 "sherry_gemm_plan_override": ([ci, ci, ci, ci], ci),
+                "sherry_linear_plan": ([i64, i64, i64, ip, ip, ip, ip, ip, ip], ci),
                 "sherry_quantize_pack": ([vp, i64, i64, vp, vp, vp], ci),
                 "sherry_quantize_act": ([vp, i64, i64, vp, vp, vp], ci),
                 "sherry_gemm": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
@@ -125,6 +126,16 @@ def plan(M: int, N: int, K: int) -> dict:
     path, grid, block, splits, lds = (v.value for v in vals)
     return {"path": PATHS.get(path, str(path)), "grid": grid,
             "block": block, "splits": splits, "lds_bytes": lds}
+
+
+def linear_plan(M: int, N: int, K: int) -> dict:
+    """Launch plan of sherry_linear's product for a shape, and whether the
+    quantization is fused into it (one launch)."""
+    vals = [ctypes.c_int() for _ in range(6)]
+    _check(lib().sherry_linear_plan(M, N, K, *[ctypes.byref(v) for v in vals]), "sherry_linear_plan")
+    path, grid, block, splits, lds, fused = (v.value for v in vals)
+    return {"path": PATHS.get(path, str(path)), "grid": grid, "block": block,
+            "splits": splits, "lds_bytes": lds, "fused": bool(fused)}
 
 
 PATHS = {0: "lut_gemv", 1: "decode_mfma", 2: "decode_mfma_gemv"}

@@ -56,8 +56,9 @@ std::atomic<int> g_ovr_path{-1}, g_ovr_rw{0}, g_ovr_ch{0}, g_ovr_splits{0};
 // per row tile and no K-split already keep >= 1024 waves streaming; smaller
 // N uses 4 waves per row tile and splits K until there are >= 1024 waves and
 // each wave has at most ~3 k-tiles (measured on MI355X at the LLaMA shapes).
+GemmPlan mfma_gemv_plan_of(int M, int N, int K, int kw, int splits);
+
 GemmPlan plan_mfma_gemv(int M, int N, int K) {
-  GemmPlan p{};
   const int KT = k_tiles(K), RT = row_tiles(N);
   const int ovr_kw = g_ovr_rw.load();
   int kw = ovr_kw == 4 || ovr_kw == 8 || ovr_kw == 16 ? ovr_kw : (RT >= 128 ? 8 : 4);
@@ -72,6 +73,14 @@ GemmPlan plan_mfma_gemv(int M, int N, int K) {
     const int max_splits = KT / kw > 0 ? KT / kw : 1;   // >= one k-tile per wave
     if (splits > max_splits) splits = max_splits;
   }
+  return mfma_gemv_plan_of(M, N, K, kw, splits);
+}
+
+// The matrix-core GEMV's plan for kw waves per row tile and (at most)
+// `splits` K-splits.
+GemmPlan mfma_gemv_plan_of(int M, int N, int K, int kw, int splits) {
+  GemmPlan p{};
+  const int KT = k_tiles(K), RT = row_tiles(N);
   if (splits > KT) splits = KT;
   if (splits < 1) splits = 1;
   const int kt_per_split = (KT + splits - 1) / splits;
@@ -231,9 +240,29 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Scratch of sherry_linear: q [M,K] and s_x [M] when the quantization is
 // not fused into the product (any content; not kept zero).
-size_t linear_scratch(int M, int N, int K, GemmPlan* plan_out, bool* fused_out) {
+// sherry_linear's plan: the product's, except on the matrix-core GEMV with a
+// K-split when the quantization is fused.  Every fused workgroup reads its
+// tokens' whole fp32 rows for the scales, so that form takes twice the waves
+// per row tile and, from 8 K-splits on, half the splits (measured on MI355X:
+// M=1, K=11008, N=4096 8.2 -> 7.2 us; M=4, K=N=4096 8.1 -> 7.8 us).  It keeps
+// a K-split, so the workspace it needs is the product's.
+GemmPlan plan_linear(int M, int N, int K, bool* fused_out) {
   const GemmPlan plan = plan_gemm(M, N, K);
-  const bool fused = mfma_gemv_fusable(plan, M, K) || lut_gemv_fusable(plan, M, K);
+  bool fused = mfma_gemv_fusable(plan, M, K) || lut_gemv_fusable(plan, M, K);
+  GemmPlan out = plan;
+  if (fused && plan.path == 2 && plan.splits > 1 && g_ovr_rw.load() == 0 && g_ovr_splits.load() == 0) {
+    const int kw = plan.rw * 2 > 16 ? 16 : plan.rw * 2;
+    const int splits = plan.splits >= 8 ? plan.splits / 2 : plan.splits;
+    const GemmPlan f = mfma_gemv_plan_of(M, N, K, kw, splits);
+    if (f.splits > 1 && mfma_gemv_fusable(f, M, K)) out = f;
+  }
+  if (fused_out) *fused_out = fused;
+  return out;
+}
+
+size_t linear_scratch(int M, int N, int K, GemmPlan* plan_out, bool* fused_out) {
+  bool fused = false;
+  const GemmPlan plan = plan_linear(M, N, K, &fused);
   if (plan_out) *plan_out = plan;
   if (fused_out) *fused_out = fused;
   return fused ? 0 : round256((size_t)M * K) + round256((size_t)M * 4);
@@ -275,6 +304,20 @@ sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path, int* 
   if (block) *block = p.block;
   if (splits) *splits = p.splits;
   if (lds_bytes) *lds_bytes = p.lds_bytes;
+  return SHERRY_OK;
+}
+
+sherry_status sherry_linear_plan(int64_t M, int64_t N, int64_t K, int* path, int* grid, int* block,
+                                 int* splits, int* lds_bytes, int* fused) {
+  if (!shape_ok(M, N, K)) return SHERRY_ERR_SHAPE;
+  bool f = false;
+  const GemmPlan p = plan_linear((int)M, (int)N, (int)K, &f);
+  if (path) *path = p.path;
+  if (grid) *grid = p.grid;
+  if (block) *block = p.block;
+  if (splits) *splits = p.splits;
+  if (lds_bytes) *lds_bytes = p.lds_bytes;
+  if (fused) *fused = f ? 1 : 0;
   return SHERRY_OK;
 }
 

@@ -201,6 +201,19 @@ sherry_status sherry_gemm_plan(int64_t M, int64_t N, int64_t K, int* path,
                                int* grid, int* block, int* splits,
                                int* lds_bytes);
 
+/* Launch plan of sherry_linear's product for a shape, with the same outputs
+ * as sherry_gemm_plan, plus fused = 1 when the quantization runs inside the
+ * product kernel (one launch), else 0 (sherry_quantize_act first, then the
+ * product on the plan above).  The fused form on path 2 with a K-split takes
+ * twice the waves per row tile of sherry_gemm's plan and, from 8 K-splits on,
+ * half the splits: its workgroups each read their tokens' whole fp32 rows
+ * for the scales, so fewer, wider workgroups cost less.  Host-only, pure;
+ * follows sherry_gemm_plan_override (with rw or splits set, the fused form
+ * keeps that plan). */
+sherry_status sherry_linear_plan(int64_t M, int64_t N, int64_t K, int* path,
+                                 int* grid, int* block, int* splits,
+                                 int* lds_bytes, int* fused);
+
 /* Tuning knob for benchmark sweeps and tests (host-only).  Replaces the
  * built-in launch plan for shapes with M <= 128 for every later call in this
  * process (M > 128 always uses path 1):

@@ -166,6 +166,39 @@ def test_python_wrapper_rejects_cpu_and_noncontiguous():
         bw.quantize_act(torch.zeros(1, 128))
 
 
+def test_linear_plan():
+    """sherry_linear's plan: the product's, except that the fused form on the
+    matrix-core GEMV with a K-split takes twice the waves per row tile and,
+    from 8 K-splits on, half the splits; it keeps a K-split, so it needs the
+    product's workspace."""
+    for M, N, K in [(1, 4096, 4096), (4, 4096, 4096), (1, 4096, 11008), (1, 11008, 4096),
+                    (1, 256, 256), (16, 4096, 4096), (512, 14336, 4096), (2, 4096, 11008)]:
+        g, lp = bw.plan(M, N, K), bw.linear_plan(M, N, K)
+        assert lp["fused"] == (bw.linear_scratch_bytes(M, N, K) == 0)
+        if not lp["fused"] or g["path"] != "decode_mfma_gemv" or g["splits"] == 1:
+            assert {k: v for k, v in lp.items() if k != "fused"} == g, (M, N, K)
+            continue
+        assert lp["path"] == g["path"] and lp["splits"] > 1
+        assert lp["block"] == min(1024, 2 * g["block"])
+        want = g["splits"] // 2 if g["splits"] >= 8 else g["splits"]
+        KT = (K + 127) // 128
+        assert lp["splits"] == -(-KT // -(-KT // want))            # as the product rounds splits
+        assert lp["grid"] == (N + 63) // 64 * lp["splits"]
+        # fusable: at most 32 k-tiles per split held in LDS as int8
+        assert -(-KT // lp["splits"]) <= 32
+    # LLaMA-7B down projection (K=11008): 8 splits of 4 waves -> 4 splits of 8 waves
+    g, lp = bw.plan(1, 4096, 11008), bw.linear_plan(1, 4096, 11008)
+    assert (g["splits"], g["block"]) == (8, 256) and (lp["splits"], lp["block"]) == (4, 512)
+    # an override of waves or splits keeps the product's plan for the fused form
+    try:
+        bw.plan_override("decode_mfma_gemv", rw=4, splits=4)
+        lp = bw.linear_plan(1, 4096, 4096)
+        assert (lp["block"], lp["splits"], lp["fused"]) == (256, 4, True)
+    finally:
+        bw.plan_override()
+    assert bw.lib().sherry_linear_plan(1, 98, 128, None, None, None, None, None, None) == SHAPE
+
+
 def test_linear_scratch_and_validation():
     L = bw.lib()
     # fused (M <= 4, M*K <= 16384): no scratch
