@@ -271,6 +271,98 @@ def test_workload_5_prefill_sampled(orc):
     _workload_check(orc, "5", sample_rows=rows)
 
 
+# ----------------------------------------------- the shape rule's maxima
+def test_max_k(orc):
+    """K = 2^20 (8192 k-tiles per row; the GEMV's K-split plan, the lookup
+    tables and the unfused sherry_linear), against the whole oracle product."""
+    M, N, K = 1, 64, 1 << 20
+    W = synth.weights(N, K, 0.02, False, seed=7001)
+    x = synth.activations(M, K, seed=7002)
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    acc, y = orc.gemm(q, s, T, alpha)
+    packed, galpha = gpu_pack(W)
+    del W
+    assert np.array_equal(packed.cpu().numpy(), orc.pack(T)), "packed codes"
+    gq, gs = bw.quantize_act(x.cuda())
+    for path in (None, "lut_gemv"):
+        try:
+            bw.plan_override(path)
+            _say(f"max K: M={M} N={N} K={K} path {path}: {bw.plan(M, N, K)}")
+            gacc = bw.gemm_i32(gq, packed, N, K).cpu().numpy()
+            gy = bw.gemm(gq, gs, packed, galpha, N, K).cpu().numpy()
+        finally:
+            bw.plan_override()
+        assert np.array_equal(gacc, acc), f"acc ({path})"
+        assert_y_close(gy, y)
+    _say(f"max K: linear, scratch {bw.linear_scratch_bytes(M, N, K)}")
+    gy = bw.linear(x.cuda(), packed, galpha, N, K).cpu().numpy()
+    assert_y_close(gy, y)
+
+
+def test_max_n(orc):
+    """N = 2^20 (16384 row tiles, one ragged k-tile of K = 16), every small-M
+    path, against the whole oracle product."""
+    M, N, K = 3, 1 << 20, 16
+    W = synth.weights(N, K, 0.02, False, seed=7011)
+    x = synth.activations(M, K, seed=7012)
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    acc, y = orc.gemm(q, s, T, alpha)
+    packed, galpha = gpu_pack(W)
+    del W
+    assert np.array_equal(packed.cpu().numpy(), orc.pack(T)), "packed codes"
+    gq, gs = bw.quantize_act(x.cuda())
+    for path in (None, "lut_gemv", "decode_mfma"):
+        try:
+            bw.plan_override(path)
+            _say(f"max N: M={M} N={N} K={K} path {path}: {bw.plan(M, N, K)}")
+            gacc = bw.gemm_i32(gq, packed, N, K).cpu().numpy()
+            gy = bw.gemm(gq, gs, packed, galpha, N, K).cpu().numpy()
+        finally:
+            bw.plan_override()
+        assert np.array_equal(gacc, acc), f"acc ({path})"
+        assert_y_close(gy, y)
+    _say("max N: linear (fused)")
+    gy = bw.linear(x.cuda(), packed, galpha, N, K).cpu().numpy()
+    assert_y_close(gy, y)
+
+
+def test_max_m(orc):
+    """M = 2^20 tokens with N = 4096, so that m*N passes 2^31 (64-bit output
+    offsets), on the prefill kernel and sherry_linear; sampled tokens, among
+    them the first and the last, against the oracle."""
+    M, N, K = 1 << 20, 4096, 16
+    W = synth.weights(N, K, 0.02, False, seed=7021)
+    x = synth.activations(M, K, seed=7022)
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    packed, galpha = gpu_pack(W)
+    del W
+    rng = np.random.default_rng(7023)
+    toks = np.unique(np.concatenate([[0, 1, 127, 128, (1 << 19) - 1, 1 << 19, (1 << 19) + 1, M - 2, M - 1],
+                                     rng.choice(M, 55, replace=False)]))
+    assert (toks.astype(np.int64) * N).max() > 2 ** 31
+    acc = orc.gemm_i32(np.ascontiguousarray(q[toks]), T)
+    y = orc.epilogue(acc, np.ascontiguousarray(s[toks]), alpha)
+    xg = x.cuda()
+    gq, gs = bw.quantize_act(xg)
+    assert np.array_equal(gq[torch.from_numpy(toks).cuda()].cpu().numpy(), q[toks]), "q (sampled)"
+    ti = torch.from_numpy(toks).cuda()
+    _say(f"max M: M={M} N={N} K={K}: {bw.plan(M, N, K)}")
+    gacc = bw.gemm_i32(gq, packed, N, K)
+    assert np.array_equal(gacc[ti].cpu().numpy(), acc), "acc (sampled)"
+    del gacc
+    gy = bw.gemm(gq, gs, packed, galpha, N, K)
+    assert_y_close(gy[ti].cpu().numpy(), y)
+    del gy
+    _say("max M: linear")
+    gy = bw.linear(xg, packed, galpha, N, K)
+    assert_y_close(gy[ti].cpu().numpy(), y)
+    del gy
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------- fused quantization + product
 def _linear_check(orc, x, packed, T, alpha, galpha, N, K, what):
     q, s = orc.act_quant(x.numpy())
