@@ -29,6 +29,11 @@ FLAGS = [
 # MFMA accumulators in arch VGPRs: the matrix ops then accumulate in place
 # instead of shuffling accumulation registers every k-step
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+# The GEMV kernels' eight leading arguments (packed, x, xf, M, N, K, splits,
+# kt_per_split: 11 SGPRs) preloaded into SGPRs at dispatch instead of read
+# from the kernel-argument segment by the first instructions
+PRELOAD = {"mfma_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+           "lut_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"]}
 
 
 def _filter(text: str) -> str:
@@ -42,7 +47,7 @@ def build(verbose: bool = False) -> str:
         procs = []
         for src in SOURCES:
             obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-            cmd = [HIPCC, *FLAGS, *VGPR_FORM, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *FLAGS, *VGPR_FORM, *PRELOAD.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,

@@ -64,15 +64,19 @@ __device__ __forceinline__ short2_t pair_of(int x0, int x1, int j) {
 }
 
 template <int MP, int CH, int RW, int KW, bool FQ>
-__global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int splits,
-                                                                 int kt_per_split) {
+__global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* packed, const int8_t* x,
+                                                                 const float* xf, int M, int N, int K,
+                                                                 int splits, int kt_per_split,
+                                                                 const float* s_x, const float* alpha,
+                                                                 float* y, int32_t* acc_out,
+                                                                 int32_t* partials) {
+  const GemmArgs a = gemv_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
   constexpr int NT = 64 * RW * KW;
   constexpr int CPW = (CH + KW - 1) / KW;        // k-tiles per wave per stage
   extern __shared__ uint32_t lut[];               // tables (dynamic LDS)
   __shared__ float fq_red[FQ ? RW * KW * 2 * MP : 1];   // fused form: partial maxima
   __shared__ float fq_s[FQ ? 2 * MP : 1];               //   and the per-token scales
 
-  const int M = a.M, N = a.N, K = a.K;
   const int KT = k_tiles(K), RT = row_tiles(N);
   const int g = blockIdx.x / splits;
   const int s = blockIdx.x - g * splits;
@@ -279,8 +283,8 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(GemmArgs a, int 
 
 template <int MP, int CH, int RW, int KW, bool FQ>
 hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((lut_gemv_kernel<MP, CH, RW, KW, FQ>), dim3(p.grid), dim3(64 * RW * KW),
-                     p.lds_bytes, stream, a, p.splits, p.kt_per_split);
+  launch_gemv_kernel(lut_gemv_kernel<MP, CH, RW, KW, FQ>, dim3(p.grid), dim3(64 * RW * KW), p.lds_bytes,
+                     stream, a, p.splits, p.kt_per_split);
   return hipGetLastError();
 }
 

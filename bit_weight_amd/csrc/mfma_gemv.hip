@@ -110,7 +110,12 @@ constexpr bool quad_x(int MT, int MB) { return MT == 16 && MB >= 1; }
 // FS = fused form: float4 loads per thread covering the tokens' rows
 // (>= M*K / (4 * 64 * KW); the launch picks the smallest power of two).
 template <int KW, int MT, int MB, bool FQ, int FMT, int ST, int FS = 1>
-__global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int splits, int kt_per_split) {
+__global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packed, const int8_t* x,
+                                                            const float* xf, int M, int N, int K, int splits,
+                                                            int kt_per_split, const float* s_x,
+                                                            const float* alpha, float* y, int32_t* acc_out,
+                                                            int32_t* partials) {
+  const GemmArgs a = gemv_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
   static_assert(MB == 1 || (MT == 16 && !FQ), "several token blocks are whole blocks of 16");
   constexpr bool XQ = !FQ && quad_x(MT, MB);
   constexpr int kStages = ST;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(GemmArgs a, int spli
   __shared__ __attribute__((aligned(16))) uint32_t qs[FQ ? MT * QS / 4 : 4];
   __shared__ float sred[FQ ? KW * MT + MT : 1];                          // partial maxima, scales
 
-  const int M = a.M, N = a.N, K = a.K, KT = k_tiles(K);
+  const int KT = k_tiles(K);
   const int rt = blockIdx.x / splits;
   const int s = blockIdx.x - rt * splits;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -413,8 +418,7 @@ hipError_t launch_fused_fs(const GemmPlan& p, const GemmArgs& a, hipStream_t str
     if (need > FS) return launch_fused_fs<KW, MT, 2 * FS>(p, a, stream, need);
   }
   if (need > FS) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemv_kernel<KW, MT, 1, true, 0, 4, FS>), dim3(p.grid), dim3(64 * KW), 0, stream, a,
-                     p.splits, p.kt_per_split);
+  launch_gemv_kernel(mfma_gemv_kernel<KW, MT, 1, true, 0, 4, FS>, dim3(p.grid), dim3(64 * KW), 0, stream, a, p.splits, p.kt_per_split);
   return hipGetLastError();
 }
 
@@ -429,14 +433,14 @@ hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     if (a.M <= 4) return launch_fused_fs<KW, 4, 1>(p, a, stream, need);
     return hipErrorInvalidValue;
   } else {
-    if (a.M <= 1) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 1, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 2) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 2, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 4) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 4, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 8) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 16) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, 1, false, FMT, 4>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    if (a.M <= 1) launch_gemv_kernel(mfma_gemv_kernel<KW, 1, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 2) launch_gemv_kernel(mfma_gemv_kernel<KW, 2, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 4) launch_gemv_kernel(mfma_gemv_kernel<KW, 4, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 8) launch_gemv_kernel(mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 16) launch_gemv_kernel(mfma_gemv_kernel<KW, 16, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
     else if constexpr (FMT == 0 && KW <= 8) {   // 16 waves leave too few registers for two blocks
-      if (a.M <= 32) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, 2, false, 0, 3>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
-      else if (a.M <= kGemvMaxM) hipLaunchKernelGGL((mfma_gemv_kernel<KW, 16, 4, false, 0, 2>), grid, block, 0, stream, a, p.splits, p.kt_per_split);
+      if (a.M <= 32) launch_gemv_kernel(mfma_gemv_kernel<KW, 16, 2, false, 0, 3>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+      else if (a.M <= kGemvMaxM) launch_gemv_kernel(mfma_gemv_kernel<KW, 16, 4, false, 0, 2>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
       else return hipErrorInvalidValue;
     } else {
       return hipErrorInvalidValue;
