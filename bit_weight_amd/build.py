@@ -29,11 +29,14 @@ FLAGS = [
 # MFMA accumulators in arch VGPRs: the matrix ops then accumulate in place
 # instead of shuffling accumulation registers every k-step
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-# The GEMV kernels' eight leading arguments (packed, x, xf, M, N, K, splits,
-# kt_per_split: 11 SGPRs) preloaded into SGPRs at dispatch instead of read
-# from the kernel-argument segment by the first instructions
+# Kernel arguments preloaded into SGPRs at dispatch instead of read from the
+# kernel-argument segment by the first instructions: the product kernels'
+# eight leading ones (packed, x, xf, M, N, K and two plan integers, 11
+# SGPRs), the quantizer's four (x, q, s_x, K)
 PRELOAD = {"mfma_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
-           "lut_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"]}
+           "lut_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+           "mfma_gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+           "pack.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"]}
 
 
 def _filter(text: str) -> str:

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
                                                                  const float* s_x, const float* alpha,
                                                                  float* y, int32_t* acc_out,
                                                                  int32_t* partials) {
-  const GemmArgs a = gemv_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
+  const GemmArgs a = product_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
   constexpr int NT = 64 * RW * KW;
   constexpr int CPW = (CH + KW - 1) / KW;        // k-tiles per wave per stage
   extern __shared__ uint32_t lut[];               // tables (dynamic LDS)
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
 
 template <int MP, int CH, int RW, int KW, bool FQ>
 hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  launch_gemv_kernel(lut_gemv_kernel<MP, CH, RW, KW, FQ>, dim3(p.grid), dim3(64 * RW * KW), p.lds_bytes,
+  launch_product_kernel(lut_gemv_kernel<MP, CH, RW, KW, FQ>, dim3(p.grid), dim3(64 * RW * KW), p.lds_bytes,
                      stream, a, p.splits, p.kt_per_split);
   return hipGetLastError();
 }

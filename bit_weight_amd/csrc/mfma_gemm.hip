@@ -153,7 +153,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-__global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_tiles) {
+__global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* packed, const int8_t* x,
+                                                             const float* xf, int M, int N, int K,
+                                                             int n_tiles, int /*unused*/, const float* s_x,
+                                                             const float* alpha, float* y, int32_t* acc_out,
+                                                             int32_t* partials) {
+  const GemmArgs a = product_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
   // the activation buffers [buffer][parity]; after the main loop the
   // epilogue tile reuses them
   // (32-bit words: every view below is a character type or 32-bit lanes)
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(GemmArgs a, int n_t
   __shared__ __attribute__((aligned(16))) uint2 dec2[1024];
   __shared__ float sxs[kBM];   // s_x of this tile's rows (epilogue)
 
-  const int M = a.M, N = a.N, K = a.K, KT = k_tiles(K), RT = row_tiles(N);
+  const int KT = k_tiles(K), RT = row_tiles(N);
   // tile id -> (m tile, n tile): consecutive ids of one XCD share n tiles
   const int id = blockIdx.x;
   const int mt_count = (M + kBM - 1) / kBM;
@@ -392,7 +397,7 @@ int mfma_gemm_grid(int M, int N) {
 
 hipError_t launch_mfma_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   const int nt = (a.N + kBN - 1) / kBN;
-  hipLaunchKernelGGL(mfma_gemm_kernel, dim3(p.grid), dim3(kThreads), 0, stream, a, nt);
+  launch_product_kernel(mfma_gemm_kernel, dim3(p.grid), dim3(kThreads), 0, stream, a, nt, 0);
   return hipGetLastError();
 }
 

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
                                                             int kt_per_split, const float* s_x,
                                                             const float* alpha, float* y, int32_t* acc_out,
                                                             int32_t* partials) {
-  const GemmArgs a = gemv_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
+  const GemmArgs a = product_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
   static_assert(MB == 1 || (MT == 16 && !FQ), "several token blocks are whole blocks of 16");
   constexpr bool XQ = !FQ && quad_x(MT, MB);
   constexpr int kStages = ST;
@@ -418,7 +418,7 @@ hipError_t launch_fused_fs(const GemmPlan& p, const GemmArgs& a, hipStream_t str
     if (need > FS) return launch_fused_fs<KW, MT, 2 * FS>(p, a, stream, need);
   }
   if (need > FS) return hipErrorInvalidValue;
-  launch_gemv_kernel(mfma_gemv_kernel<KW, MT, 1, true, 0, 4, FS>, dim3(p.grid), dim3(64 * KW), 0, stream, a, p.splits, p.kt_per_split);
+  launch_product_kernel(mfma_gemv_kernel<KW, MT, 1, true, 0, 4, FS>, dim3(p.grid), dim3(64 * KW), 0, stream, a, p.splits, p.kt_per_split);
   return hipGetLastError();
 }
 
@@ -433,14 +433,14 @@ hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     if (a.M <= 4) return launch_fused_fs<KW, 4, 1>(p, a, stream, need);
     return hipErrorInvalidValue;
   } else {
-    if (a.M <= 1) launch_gemv_kernel(mfma_gemv_kernel<KW, 1, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 2) launch_gemv_kernel(mfma_gemv_kernel<KW, 2, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 4) launch_gemv_kernel(mfma_gemv_kernel<KW, 4, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 8) launch_gemv_kernel(mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 16) launch_gemv_kernel(mfma_gemv_kernel<KW, 16, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    if (a.M <= 1) launch_product_kernel(mfma_gemv_kernel<KW, 1, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 2) launch_product_kernel(mfma_gemv_kernel<KW, 2, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 4) launch_product_kernel(mfma_gemv_kernel<KW, 4, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 8) launch_product_kernel(mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 16) launch_product_kernel(mfma_gemv_kernel<KW, 16, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
     else if constexpr (FMT == 0 && KW <= 8) {   // 16 waves leave too few registers for two blocks
-      if (a.M <= 32) launch_gemv_kernel(mfma_gemv_kernel<KW, 16, 2, false, 0, 3>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-      else if (a.M <= kGemvMaxM) launch_gemv_kernel(mfma_gemv_kernel<KW, 16, 4, false, 0, 2>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+      if (a.M <= 32) launch_product_kernel(mfma_gemv_kernel<KW, 16, 2, false, 0, 3>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+      else if (a.M <= kGemvMaxM) launch_product_kernel(mfma_gemv_kernel<KW, 16, 4, false, 0, 2>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
       else return hipErrorInvalidValue;
     } else {
       return hipErrorInvalidValue;

@@ -50,24 +50,25 @@ struct GemmArgs {
   int32_t* partials;   // workspace: zero-filled 64-bit accumulators [M,N] for K-splits
 };
 
-// The GEMV kernels take their arguments as pointers and scalars, not as a
-// GemmArgs struct, with the ones their first instructions need in front:
-// packed, x, xf, M, N, K, splits, kt_per_split, then s_x, alpha, y, acc,
+// The product kernels take their arguments as pointers and scalars, not as
+// a GemmArgs struct, with the ones their first instructions need in front:
+// packed, x, xf, M, N, K, two plan integers (the GEMVs: splits and k-tiles
+// per split; the prefill GEMM: n tiles and 0), then s_x, alpha, y, acc,
 // partials.  The build has the leading ones preloaded into SGPRs at
 // dispatch (gfx950 kernel-argument preload), which removes a memory round
 // trip from the start of every launch; a struct argument cannot be
 // preloaded.
 template <typename Kernel>
-inline void launch_gemv_kernel(Kernel kernel, dim3 grid, dim3 block, size_t lds_bytes,
-                               hipStream_t stream, const GemmArgs& a, int splits, int kt_per_split) {
-  hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, a.packed, a.x, a.xf, a.M, a.N, a.K, splits,
-                     kt_per_split, a.s_x, a.alpha, a.y, a.acc, a.partials);
+inline void launch_product_kernel(Kernel kernel, dim3 grid, dim3 block, size_t lds_bytes,
+                                  hipStream_t stream, const GemmArgs& a, int plan0, int plan1) {
+  hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, a.packed, a.x, a.xf, a.M, a.N, a.K, plan0,
+                     plan1, a.s_x, a.alpha, a.y, a.acc, a.partials);
 }
 
-// The GemmArgs a GEMV kernel rebuilds from its arguments.
-__device__ __forceinline__ GemmArgs gemv_args(const uint8_t* packed, const int8_t* x, const float* xf,
-                                              int M, int N, int K, const float* s_x, const float* alpha,
-                                              float* y, int32_t* acc, int32_t* partials) {
+// The GemmArgs a product kernel rebuilds from its arguments.
+__device__ __forceinline__ GemmArgs product_args(const uint8_t* packed, const int8_t* x, const float* xf,
+                                                 int M, int N, int K, const float* s_x, const float* alpha,
+                                                 float* y, int32_t* acc, int32_t* partials) {
   GemmArgs a{};
   a.packed = packed;
   a.x = x;
