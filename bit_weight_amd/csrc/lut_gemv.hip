@@ -120,8 +120,7 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
 #pragma unroll 4
         for (int e = threadIdx.x; e < K4; e += NT) am = fmaxf(am, amax4(xr[e]));
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      am = wave_max(am);
       if (lane == 0) fq_red[wave * 2 * MP + m] = am;
     }
     __syncthreads();

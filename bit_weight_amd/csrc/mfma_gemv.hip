@@ -239,8 +239,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) am[m] = fmaxf(am[m], __shfl_xor(am[m], off, 64));
+      am[m] = wave_max(am[m]);
       if (lane == 0) sred[q * MT + m] = am[m];
     }
     __syncthreads();

@@ -133,8 +133,7 @@ __device__ __forceinline__ float amax4(const float4 v) {
 }
 
 __device__ __forceinline__ float block_amax(float amax, float* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
   __syncthreads();
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));

@@ -81,6 +81,32 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[5], int j) {
   return __builtin_amdgcn_alignbit(w[d + 1], w[d], sh) & 31u;
 }
 
+// x as read from another lane of its 16-lane row by DPP control CTRL.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x),
+                                                               __builtin_bit_cast(int, x), CTRL, 0xF,
+                                                               0xF, false));
+}
+
+// Maximum over the 64 lanes of a wave, the same value in every lane (all
+// lanes active).  Within each 16-lane row by DPP permutes (swap neighbours,
+// swap pairs, rotate by 4, rotate by 8), then over the four rows' values
+// read from one lane each.  A shuffle (ds_bpermute) would cost an LDS round
+// trip per step; these are VALU operations.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_move<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_move<0x124>(v));   // row_ror:4
+  v = fmaxf(v, dpp_move<0x128>(v));   // row_ror:8
+  const int u = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Workgroup barrier that orders only LDS accesses.  __syncthreads() also
 // orders global memory, so it waits for every global load in flight; this
 // one leaves prefetched loads outstanding across the barrier.
