@@ -271,6 +271,73 @@ def test_workload_5_prefill_sampled(orc):
     _workload_check(orc, "5", sample_rows=rows)
 
 
+# ------------------------------------------------------- HIP graph capture
+@pytest.mark.parametrize("path,M,N,K", [(None, 1, 4096, 4096),        # fused step, K-split cells
+                                        (None, 8, 1024, 2048),        # quantizer + GEMV
+                                        ("lut_gemv", 3, 512, 1152),   # fused lookup tables
+                                        (None, 200, 512, 640)])       # quantizer + prefill
+def test_graph_replays_match_eager(orc, path, M, N, K):
+    """sherry_linear and sherry_gemm captured into one HIP graph: every replay
+    (with eager calls and synchronizations between replays, and inputs
+    rewritten in place) is bit-identical to eager calls on the same inputs,
+    and the K-split workspace stays zero throughout."""
+    W = synth.weights(N, K, 0.02, False, seed=8100 + N)
+    packed, galpha = gpu_pack(W)
+    xs = [synth.activations(M, K, seed=8200 + i).cuda() for i in range(3)]
+    try:
+        bw.plan_override(path)
+        _say(f"graph: path {path} M={M} N={N} K={K} linear plan {bw.linear_plan(M, N, K)}")
+        ws = torch.zeros(max(bw.workspace_bytes(M, N, K), 256), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(max(bw.linear_scratch_bytes(M, N, K), 256), dtype=torch.uint8, device="cuda")
+        x = xs[0].clone()
+        q, s = bw.quantize_act(x)
+        y1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        y2 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+        def calls():
+            bw.linear(x, packed, galpha, N, K, out=y1, workspace=ws, scratch=sc)
+            bw.gemm(q, s, packed, galpha, N, K, out=y2, workspace=ws)
+
+        def eager(xv):
+            qv, sv = bw.quantize_act(xv)
+            e1 = bw.linear(xv, packed, galpha, N, K, workspace=ws,
+                           scratch=torch.empty_like(sc))
+            e2 = bw.gemm(qv, sv, packed, galpha, N, K, workspace=ws)
+            torch.cuda.synchronize()
+            return e1.clone(), e2.clone()
+
+        calls()                           # warm up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                calls()
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        for r in range(6):
+            xv = xs[r % 3]
+            x.copy_(xv)
+            qv, sv = bw.quantize_act(xv)
+            q.copy_(qv)
+            s.copy_(sv)
+            torch.cuda.synchronize()
+            e1, e2 = eager(xv)            # eager work between replays
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y1, e1), f"linear, replay {r}"
+            assert torch.equal(y2, e2), f"gemm, replay {r}"
+            assert int(ws.count_nonzero()) == 0, f"workspace left non-zero, replay {r}"
+        # and the eager results are the oracle's
+        T, alpha = orc.quantize(W.numpy())
+        qo, so = orc.act_quant(xs[2].cpu().numpy())
+        _, yo = orc.gemm(qo, so, T, alpha)
+        assert_y_close(y1.cpu().numpy(), yo)
+    finally:
+        bw.plan_override()
+
+
 # ----------------------------------------------- the shape rule's maxima
 def test_max_k(orc):
     """K = 2^20 (8192 k-tiles per row; the GEMV's K-split plan, the lookup
