@@ -1,4 +1,4 @@
-// Small-M (decode and short chunks, M <= 64) product on the matrix cores:
+// Small-M (decode and short chunks, M <= 64 per launch) product on the matrix cores:
 // the 5-bit codes are decoded to int8 {-1,0,+1} in registers and contracted
 // with the int8 activations by v_mfma_i32_16x16x64_i8, the M tokens padded
 // to whole blocks of the instruction's 16 rows (one decoded operand feeds
@@ -38,9 +38,9 @@
 //    reads the A operands from there; this saves the quantizer's launch and
 //    its round trip through memory on the decode path.
 //  * Codes and activations are prefetched four k-tiles ahead into four
-//    register stages used in turn, so each wave keeps ~5 KB of its codes in
-//    flight (HBM streaming needs bytes in flight x latency to cover the
-//    bandwidth).
+//    register stages used in turn (three or two with several token blocks),
+//    so each wave keeps ~5 KB of its codes in flight (HBM streaming needs
+//    bytes in flight x latency to cover the bandwidth).
 #include "sherry_device.h"
 #include "sherry_launch.h"
 
