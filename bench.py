@@ -21,8 +21,9 @@ quantization is fused into the product (as it is for this workload), else
 the product kernel the launch plan picks; "prefill" holds the M=512 decode + int8 MFMA
 product against the 5.0 POP/s int8 peak; "workloads" holds every workload's
 kernel time, and for M <= 16 the time of each small-M path (lookup-table
-GEMV and matrix-core GEMV); "grouped_qkv" times three projections as one call
-on stacked packed weights against three calls; "two_bit_baseline" times the
+GEMV and matrix-core GEMV); "grouped_qkv" and "grouped_gate_up" time three
+(two) projections of one x as one call on stacked packed weights against
+separate calls; "two_bit_baseline" times the
 same ternary weights in the plain 2-bit packing.  "cpu_baseline" times the
 CPU oracle (single thread) on a bounded sample of the same workload.
 """
@@ -243,15 +244,16 @@ def two_bit_bench(torch, bw, synth, five_bit_us: dict):
     return res
 
 
-def grouped_bench(torch, bw, synth):
-    """q/k/v-style group at the LLaMA-7B attention shape: three 4096 x 4096
-    projections of one token, as one sherry_linear call on the stacked packed
-    weights versus three calls (rotating copies, as for the step)."""
-    w = synth.WORKLOADS["2a"]
+def grouped_bench(torch, bw, synth, name: str = "2a", G: int = 3):
+    """G projections of one token sharing x, as one sherry_linear call on the
+    stacked packed weights versus G calls (rotating copies, as for the step):
+    q/k/v at the LLaMA-7B attention shape (workload 2a, G = 3) or gate/up at
+    its MLP shape (workload 3a, N = 11008, G = 2)."""
+    w = synth.WORKLOADS[name]
     W = synth.workload_weights(w).cuda()
     p1, a1 = bw.quantize_pack(W)
     del W
-    G, nb = 3, w.packed_bytes
+    nb = w.packed_bytes
     packed, alpha = bw.concat_packed([(p1, a1)] * G, [w.N] * G, w.K)
     R = copies_for(G * nb, 0)
     packs = [packed] + [packed.clone() for _ in range(R - 1)]
@@ -265,14 +267,14 @@ def grouped_bench(torch, bw, synth):
     one, _ = graph_time(torch, lambda i: bw.linear(x, packs[i % R], alphas[i % R], G * w.N, w.K,
                                                    out=y, workspace=ws), n, reps=3)
 
-    def three(i):
+    def separate(i):
         r = i % R
         for j in range(G):
             bw.linear(x, packs[r][j * nb:(j + 1) * nb], alphas[r][j * w.N:(j + 1) * w.N], w.N, w.K,
                       out=ys[j], workspace=ws)
-    sep, _ = graph_time(torch, three, n, reps=3)
-    return {"shape": "3 x (N=4096, K=4096), M=1, fp32 x (sherry_linear)",
-            "one_call_us": round(one * 1e3, 3), "three_calls_us": round(sep * 1e3, 3),
+    sep, _ = graph_time(torch, separate, n, reps=3)
+    return {"shape": f"{G} x (N={w.N}, K={w.K}), M=1, fp32 x (sherry_linear)",
+            "one_call_us": round(one * 1e3, 3), "separate_calls_us": round(sep * 1e3, 3),
             "one_call_packed_GB_s": round(G * nb / one / 1e6, 1), "rotating_copies": R}
 
 
@@ -440,7 +442,8 @@ def main():
                                        "traffic": traffic_from_profile(
                                            "mfma_gemm", "5", p5["plan"]),
                                        "kernel": "mfma_gemm_kernel"}}
-        out["grouped_qkv"] = grouped_bench(torch, bw, synth)
+        out["grouped_qkv"] = grouped_bench(torch, bw, synth, "2a", 3)
+        out["grouped_gate_up"] = grouped_bench(torch, bw, synth, "3a", 2)
         torch.cuda.empty_cache()
         out["two_bit_baseline"] = two_bit_bench(
             torch, bw, synth, {k: v["path_us"]["decode_mfma_gemv"] for k, v in wl.items() if "path_us" in v})

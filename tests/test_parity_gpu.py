@@ -526,6 +526,29 @@ def test_grouped_projections_one_call(orc):
         assert_y_close(gy.cpu().numpy(), y)
 
 
+def test_grouped_gate_up_llama7b(orc):
+    """gate/up of the LLaMA-7B MLP (2 x [11008, 4096]) stacked into one
+    [22016, 4096] matrix: one sherry_linear gives both projections from one
+    x, bit-identical to two calls, and the oracle's."""
+    K, Ns = 4096, [11008, 11008]
+    Ws = [synth.weights(n, K, 0.02, False, seed=5300 + i) for i, n in enumerate(Ns)]
+    parts = [gpu_pack(W) for W in Ws]
+    packed, galpha = bw.concat_packed(parts, Ns, K)
+    T, alpha = orc.quantize(torch.cat(Ws).numpy())
+    assert np.array_equal(packed.cpu().numpy(), orc.pack(T)), "stacked codes"
+    del Ws
+    for M in (1, 4):
+        x = synth.activations(M, K, seed=5400 + M)
+        _say(f"gate/up M={M}: linear plan {bw.linear_plan(M, sum(Ns), K)}")
+        gy = bw.linear(x.cuda(), packed, galpha, sum(Ns), K)
+        sep = torch.cat([bw.linear(x.cuda(), p, a, n, K) for (p, a), n in zip(parts, Ns)], dim=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(gy.cpu().numpy().view(np.uint32), sep.cpu().numpy().view(np.uint32))
+        q, s = orc.act_quant(x.numpy())
+        _, y = orc.gemm(q, s, T, alpha)
+        assert_y_close(gy.cpu().numpy(), y)
+
+
 # --------------------------------------------------- 2-bit baseline format
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_pack2_parity(orc, N, K):
