@@ -109,7 +109,9 @@ constexpr bool quad_x(int MT, int MB) { return MT == 16 && MB >= 1; }
 // 32g..32g+31, through the same two transposes).  ST = register stages.
 // FS = fused form: float4 loads per thread covering the tokens' rows
 // (>= M*K / (4 * 64 * KW); the launch picks the smallest power of two).
-template <int KW, int MT, int MB, bool FQ, int FMT, int ST, int FS = 1>
+// SX = staged int8 activations: the split's x copied to LDS once, as in the
+// fused form, instead of loaded per k-tile (the launch uses it at M = 1).
+template <int KW, int MT, int MB, bool FQ, int FMT, int ST, int FS = 1, bool SX = false>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packed, const int8_t* x,
                                                             const float* xf, int M, int N, int K, int splits,
                                                             int kt_per_split, const float* s_x,
@@ -117,17 +119,19 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
                                                             int32_t* partials) {
   const GemmArgs a = product_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
   static_assert(MB == 1 || (MT == 16 && !FQ), "several token blocks are whole blocks of 16");
+  static_assert(!SX || (!FQ && MB == 1 && MT <= 4), "staged int8 activations: at most 4 tokens");
+  constexpr bool LX = FQ || SX;   // A operands read from the split's activations in LDS
   constexpr bool XQ = !FQ && quad_x(MT, MB);
   constexpr int kStages = ST;
   constexpr int NT = 64 * KW;
   constexpr int TB = FMT == 0 ? kTileBytes : kTile2Bytes;   // bytes per format tile
   __shared__ __attribute__((aligned(16))) uint32_t tbl2[FMT == 1 ? 256 : 1];
-  constexpr int QS = FQ ? kFuseMaxSpan * kTileK : 16;   // int8 activations per token in LDS
+  constexpr int QS = LX ? kFuseMaxSpan * kTileK : 16;   // int8 activations per token in LDS
   __shared__ __attribute__((aligned(16))) uint2 dec2[1024];
   __shared__ __attribute__((aligned(16))) int red[KW * MT * kRedLd];   // [wave][token][row]
   // [token][k in split] int8, held as 32-bit words: written and read only as
   // 32-bit lanes, so no access reinterprets another type's storage
-  __shared__ __attribute__((aligned(16))) uint32_t qs[FQ ? MT * QS / 4 : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t qs[LX ? MT * QS / 4 : 4];
   __shared__ float sred[FQ ? KW * MT + MT : 1];                          // partial maxima, scales
 
   const int KT = k_tiles(K);
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
     const bool in0 = ka + x_k < K, in1 = ka + x_k + 16 < K;
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
-      if constexpr (!FQ) {
+      if constexpr (!LX) {
         x0[b] = __builtin_amdgcn_raw_buffer_load_b128(rx, in0 ? x_v + 16 * b * K + ka : x_oob, 0, 0);
         x1[b] = __builtin_amdgcn_raw_buffer_load_b128(rx, in1 ? x_v + 16 * b * K + ka + 16 : x_oob, 0, 0);
       } else {
@@ -202,6 +206,26 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
     const __amdgpu_buffer_rsrc_t rxf = gemv_rsrc(a.xf, (size_t)M * (size_t)K * 4);
 #pragma unroll
     for (int j = 0; j < FS; ++j) xv[j] = __builtin_amdgcn_raw_buffer_load_b128(rxf, 16 * (tid + NT * j), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Staged form (SX, int8 x, M <= 4): the split's activations as 16-byte
+  // chunks, chunk c = tid + NT*j of [token][k in split] (span*8 per token),
+  // loaded once, coalesced and ahead of the codes, and put in LDS below;
+  // chunks past K or past the last token read as zeros
+  constexpr int XCH = SX ? (MT * kFuseMaxSpan * 8 + NT - 1) / NT : 1;
+  const int per_tok = span * 8;
+  auto chunk_token = [&](int c) { return (c >= per_tok) + (c >= 2 * per_tok) + (c >= 3 * per_tok); };
+  v4u xs[XCH];
+  if constexpr (SX) {
+#pragma unroll
+    for (int j = 0; j < XCH; ++j) {
+      const int c = tid + NT * j;
+      const int m = chunk_token(c);
+      const int jj = c - m * per_tok;   // chunk within the token's split (>= per_tok: none)
+      const int k = kt_begin * kTileK + 16 * jj;
+      xs[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, m < M && jj < per_tok && k < K ? m * K + k : x_oob,
+                                                    0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -274,6 +298,15 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
       for (int m = 0; m < MT; ++m)
         if (m < M) qs[(m * QS) / 4 + (e - e0)] = 0u;
   }
+  if constexpr (SX) {
+#pragma unroll
+    for (int j = 0; j < XCH; ++j) {
+      const int c = tid + NT * j;
+      const int m = chunk_token(c);
+      const int jj = c - m * per_tok;
+      if (m < M && jj < per_tok) *reinterpret_cast<v4u*>(&qs[(m * QS) / 4 + 4 * jj]) = xs[j];
+    }
+  }
   lds_barrier();
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
 
@@ -296,7 +329,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
       transpose4(w.y, w.w, h.y, h.w, f1);
     }
     v4i a0[MB], a1[MB];
-    if constexpr (FQ) {
+    if constexpr (LX) {
       // token l16 (zero past M), inputs 32g + 16s of this wave's i-th k-tile
       const uint32_t* src = &qs[(min(l16, M - 1) * QS + (q + KW * i) * kTileK + 32 * g) / 4];
       const v4i v0 = __builtin_bit_cast(v4i, *reinterpret_cast<const v4u*>(src));
@@ -432,7 +465,12 @@ hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     if (a.M <= 4) return launch_fused_fs<KW, 4, 1>(p, a, stream, need);
     return hipErrorInvalidValue;
   } else {
-    if (a.M <= 1) launch_product_kernel(mfma_gemv_kernel<KW, 1, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    // one token: its split's int8 x staged in LDS (measured 2-4 % faster at
+    // M=1; at M=4 the chunk loads, sized for the longest split, cost more
+    // than the per-step loads they replace)
+    if (a.M <= 1 && p.kt_per_split <= kFuseMaxSpan)
+      launch_product_kernel(mfma_gemv_kernel<KW, 1, 1, false, FMT, 4, 1, true>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
+    else if (a.M <= 1) launch_product_kernel(mfma_gemv_kernel<KW, 1, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
     else if (a.M <= 2) launch_product_kernel(mfma_gemv_kernel<KW, 2, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
     else if (a.M <= 4) launch_product_kernel(mfma_gemv_kernel<KW, 4, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
     else if (a.M <= 8) launch_product_kernel(mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
