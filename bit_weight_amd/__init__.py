@@ -145,7 +145,9 @@ PATH_IDS = {v: k for k, v in PATHS.items()}
 def plan_override(path=None, rw: int = 0, ch: int = 0, splits: int = 0) -> None:
     """Tuning knob for M <= 128: force a path ("lut_gemv", "decode_mfma",
     "decode_mfma_gemv" or None = built-in) and its launch plan (0 = built-in).
-    Above M = 16 only "decode_mfma" changes the path."""
+    Above M = 16, "decode_mfma" gives the prefill GEMM and the others the
+    GEMV.  With "decode_mfma" (any M), rw = 1 or 2 picks tiles of 64 or 128
+    tokens."""
     pid = -1 if path is None else PATH_IDS[path]
     _check(lib().sherry_gemm_plan_override(pid, rw, ch, splits), "sherry_gemm_plan_override")
 

@@ -52,23 +52,29 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 256;             // workgroup tile
-constexpr int kMT = kBM / 16;                   // 8 row blocks per wave
+constexpr int kBN = 256;                        // workgroup tile width (weight rows)
 constexpr int kNT = kTileRows / 16;             // 4 column blocks per wave (one row tile)
 constexpr int kBK = kTileK;                     // 128
-constexpr int kAStage = kBM * kBK;              // 16 KB per k-step
 constexpr int kABufs = 3;                       // activation buffers per parity
-constexpr int kACopies = kAStage / 1024 / 4;    // 1 KB copies per wave per k-step (4)
 constexpr int kThreads = 512;                   // 4 row tiles x 2 k-tile parities
 constexpr int kOutLd = kBN + 16;                // words per row of the epilogue tiles (the 4
                                                 // row groups of an MFMA block hit 4 bank quarters)
-constexpr int kLdsMain = 2 * kABufs * kAStage;  // activation buffers x parities
 constexpr int kLdsOut = 2 * 32 * kOutLd * 4;    // epilogue tiles (32 rows, both parities)
-constexpr int kLdsBytes = kLdsMain > kLdsOut ? kLdsMain : kLdsOut;
-// vector-memory ops a wave issues between a k-step's activation copy and
-// that step's barrier: the codes three steps ahead of it (2), the next
-// step's copy, and the codes four steps ahead (2)
-constexpr int kNewerLoads = 2 + kACopies + 2;
+
+// The sizes that follow from the tile height BM (128 or 64 activation rows).
+template <int BM>
+struct Tiling {
+  static constexpr int kMT = BM / 16;                  // row blocks per wave (8 or 4)
+  static constexpr int kAStage = BM * kBK;             // activation bytes per k-step
+  static constexpr int kRowsPerWave = BM / 4;          // rows each wave of a parity copies
+  static constexpr int kACopies = kRowsPerWave / 8;    // 1 KB copies (8 rows) per wave per k-step
+  static constexpr int kLdsMain = 2 * kABufs * kAStage;  // activation buffers x parities
+  static constexpr int kLdsBytes = kLdsMain > kLdsOut ? kLdsMain : kLdsOut;
+  // vector-memory ops a wave issues between a k-step's activation copy and
+  // that step's barrier: the codes three steps ahead of it (2), the next
+  // step's copy, and the codes four steps ahead (2)
+  static constexpr int kNewerLoads = 2 + kACopies + 2;
+};
 
 // Activation tile in LDS, row-major with 128-byte rows: the 16-byte chunk c
 // of row r sits at chunk position c ^ ((r >> 1) & 7).  A fragment read (16
@@ -102,21 +108,22 @@ __device__ __forceinline__ v4i mg_decode4(uint32_t v, const uint8_t* dec2) {
   return v4i{(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
 }
 
-// The 2 x 8 x 4 MFMAs of one k-step (sub-steps s = 0, 1 read A chunk 2g+s
+// The 2 x MT x 4 MFMAs of one k-step (sub-steps s = 0, 1 read A chunk 2g+s
 // of the tile at `as`, with B operands b0 / b1), and the table lookups that
 // decode the next k-step's codes (f0 / f1) into n0 / n1: those of sub-step
-// 0 spread over the last four groups of 8 MFMAs (b0 is dead by then, so n0
-// can take its registers), those of sub-step 1 after the MFMAs.  The A
+// 0 spread over the groups of 8 MFMAs of sub-step 1 (b0 is dead by then, so
+// n0 can take its registers), those of sub-step 1 after the MFMAs.  The A
 // fragments of the next two row blocks are requested before the MFMAs of
 // the current two, so the LDS latency hides behind 8 MFMAs.
-template <bool kLive>
+template <bool kLive, int kMT>
 __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kNT],
                                         const v4i (&b1)[kNT], const int8_t* as, int l16, int g,
                                         const uint32_t (&f0)[kNT], const uint32_t (&f1)[kNT],
                                         v4i (&n0)[kNT], v4i (&n1)[kNT], const uint8_t* dec2) {
-  auto frag = [&](int u) {   // u = 8 s + row block
-    return *reinterpret_cast<const v4i*>(as + a_off(16 * (u & 7) + l16, 2 * g + (u >> 3)));
+  auto frag = [&](int u) {   // u = kMT s + row block
+    return *reinterpret_cast<const v4i*>(as + a_off(16 * (u % kMT) + l16, 2 * g + u / kMT));
   };
+  constexpr int kDecPerGroup = kNT / (kMT / 2);   // sub-step-0 lookups per group of sub-step 1
   v4i a0{0, 0, 0, 0}, a1{0, 0, 0, 0};
   if constexpr (kLive) {
     a0 = frag(0);
@@ -129,10 +136,16 @@ __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kN
       p0 = frag(u + 2);
       p1 = frag(u + 3);
     }
-    if (u >= kMT) n0[(u >> 1) & 3] = mg_decode4(f0[(u >> 1) & 3], dec2);
+    if (u >= kMT) {
+#pragma unroll
+      for (int d = 0; d < kDecPerGroup; ++d) {
+        const int t = ((u - kMT) >> 1) * kDecPerGroup + d;
+        n0[t] = mg_decode4(f0[t], dec2);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kLive) {
-      const int i = u & 7;
+      const int i = u % kMT;
 #pragma unroll
       for (int c = 0; c < kNT; ++c)
         acc[i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, u < kMT ? b0[c] : b1[c], acc[i][c], 0, 0, 0);
@@ -148,17 +161,30 @@ __device__ __forceinline__ void mg_mfma(v4i (&acc)[kMT][kNT], const v4i (&b0)[kN
   for (int t = 0; t < kNT; ++t) n1[t] = mg_decode4(f1[t], dec2);
 }
 
+// 16 bytes per lane from the buffer at byte `voffset` straight into LDS at
+// dst + 16 * lane (a buffer load with LDS return).  A plain function, not a
+// lambda inside the kernel template: there the host pass rejects the LDS
+// address-space cast and silently drops the kernel's host-side stub.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, int8_t* dst, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voffset, 0, 0,
+                                           0);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, size_t bytes) {
   const int n = bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
+template <int BM>
 __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* packed, const int8_t* x,
                                                              const float* xf, int M, int N, int K,
                                                              int n_tiles, int /*unused*/, const float* s_x,
                                                              const float* alpha, float* y, int32_t* acc_out,
                                                              int32_t* partials) {
   const GemmArgs a = product_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
+  using T = Tiling<BM>;
+  constexpr int kBM = BM, kMT = T::kMT, kAStage = T::kAStage, kACopies = T::kACopies;
+  constexpr int kLdsBytes = T::kLdsBytes, kNewerLoads = T::kNewerLoads;
   // the activation buffers [buffer][parity]; after the main loop the
   // epilogue tile reuses them
   // (32-bit words: every view below is a character type or 32-bit lanes)
@@ -199,19 +225,20 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
       buffer_rsrc(a.x + (size_t)m0 * K, (size_t)(M - m0) * (size_t)K);
   const uint32_t sh = 8u * (uint32_t)g;  // bit 40g mod 32
 
-  // activations: the 4 waves of a parity copy its k-tile, 128 rows x 128
-  // bytes; copy jj of wave `wave` fills rows 32 wave + 8 jj .. +7, lane L
-  // taking chunk (L & 7) ^ swizzle of row L >> 3 (its LDS position is fixed
-  // at 16 L).  Rows past M read row M-1 (they feed only unstored rows).
+  // activations: the 4 waves of a parity copy its k-tile, BM rows x 128
+  // bytes; copy jj of wave `wave` fills rows (BM/4) wave + 8 jj .. +7, lane
+  // L taking chunk (L & 7) ^ swizzle of row L >> 3 (its LDS position is
+  // fixed at 16 L).  Rows past M read row M-1 (they feed only unstored rows).
   int a_v[kACopies];
 #pragma unroll
   for (int jj = 0; jj < kACopies; ++jj) {
-    const int row = 32 * wave + 8 * jj + (lane >> 3);
+    const int row = T::kRowsPerWave * wave + 8 * jj + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     a_v[jj] = min(row, M - 1 - m0) * K + c * 16;
   }
   // first input of a copy's chunk in its k-step: the swizzle (row >> 1) & 7
-  // of row 32 wave + 8 jj + (lane >> 3) is 4 (jj & 1) + (lane >> 4)
+  // of row (BM/4) wave + 8 jj + (lane >> 3) is 4 (jj & 1) + (lane >> 4)
+  // (BM/4 is a multiple of 16)
   int a_k[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) a_k[p] = 16 * ((lane & 7) ^ (4 * p + (lane >> 4)));
@@ -238,16 +265,14 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   // this wave's share of the activation tile of pair j into buffer b
   auto copy_a = [&](int j, int b) {
     const int ka = ktile(j) * kBK;
-    int8_t* dst = a_buf(b) + 32 * wave * kBK;
+    int8_t* dst = a_buf(b) + T::kRowsPerWave * wave * kBK;
     // (the k-step offset is added to the lane offset, not passed as the
     // scalar offset, so the descriptor's range check sees the whole offset;
     // chunks past K, in a ragged last k-tile whose codes are padding, take
     // an out-of-range offset and land as zeros)
 #pragma unroll
     for (int jj = 0; jj < kACopies; ++jj)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(dst + 8 * jj * kBK), 16,
-          ka + a_k[jj & 1] < K ? a_v[jj] + ka : a_oob, 0, 0, 0);
+      copy16_to_lds(ra, dst + 8 * jj * kBK, ka + a_k[jj & 1] < K ? a_v[jj] + ka : a_oob);
   };
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
   // the 20-bit code groups of one register stage: lane (l16, g) of block t
@@ -284,9 +309,9 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
     load_codes(min(j + 3, KJ - 1), wn, hn);
     __builtin_amdgcn_sched_barrier(0);
     if (2 * j + kh < KT)     // odd KT: the last pair has one k-tile
-      mg_mfma<true>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
+      mg_mfma<true, kMT>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
     else
-      mg_mfma<false>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
+      mg_mfma<false, kMT>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
   };
 
   // Two register stages of codes and two sets of B operands, ping-pong.
@@ -383,22 +408,32 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   }
 }
 
+template <int BM>
+hipError_t launch_tiles(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  const int nt = (a.N + kBN - 1) / kBN;
+  launch_product_kernel(mfma_gemm_kernel<BM>, dim3(p.grid), dim3(kThreads), 0, stream, a, nt, 0);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-int mfma_gemm_lds_bytes() { return kLdsBytes + 1024 * 8 + kBM * 4; }
+int mfma_gemm_lds_bytes(int bm) {
+  return (bm == 64 ? Tiling<64>::kLdsBytes : Tiling<128>::kLdsBytes) + 1024 * 8 + bm * 4;
+}
 
 int mfma_gemm_threads() { return kThreads; }
 
-int mfma_gemm_grid(int M, int N) {
-  const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
+int mfma_gemm_grid(int M, int N, int bm) {
+  const int mt = (M + bm - 1) / bm, nt = (N + kBN - 1) / kBN;
   const int per_xcd = (nt + 7) / 8;
   return 8 * per_xcd * mt;
 }
 
+// plan.rw carries the tile height in units of 64 activation rows (1 or 2).
 hipError_t launch_mfma_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  const int nt = (a.N + kBN - 1) / kBN;
-  launch_product_kernel(mfma_gemm_kernel, dim3(p.grid), dim3(kThreads), 0, stream, a, nt, 0);
-  return hipGetLastError();
+  return p.rw == 1 ? launch_tiles<64>(p, a, stream)
+         : p.rw == 2 ? launch_tiles<128>(p, a, stream)
+                     : hipErrorInvalidValue;
 }
 
 }  // namespace sherry

@@ -132,14 +132,24 @@ hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_
 
 namespace {
 // Prefill GEMM: one workgroup per 128 x 256 output tile, no K-split.
+// Tiles of 64 activation rows when that grid fits the GPU in one round
+// (<= 256 workgroups), else 128: per workgroup the 128-row tile costs half
+// the decode per multiply-add, but below ~256 tokens it leaves CUs idle
+// (M=129..256 at N=14336: 112 tiles of 128 rows).  A forced prefill path
+// with rw = 1 or 2 in the override picks the height.
 GemmPlan plan_prefill(int M, int N, int K) {
   GemmPlan p{};
+  const long long nt = (N + 255) / 256;
+  int bm = ((M + 63) / 64) * nt <= 256 ? 64 : 128;
+  const int ovr_rw = g_ovr_rw.load();
+  if (g_ovr_path.load() == 1 && (ovr_rw == 1 || ovr_rw == 2)) bm = 64 * ovr_rw;
   p.path = 1;
-  p.grid = mfma_gemm_grid(M, N);
+  p.rw = bm / 64;
+  p.grid = mfma_gemm_grid(M, N, bm);
   p.block = mfma_gemm_threads();
   p.splits = 1;
   p.kt_per_split = k_tiles(K);
-  p.lds_bytes = mfma_gemm_lds_bytes();
+  p.lds_bytes = mfma_gemm_lds_bytes(bm);
   p.ws_bytes = 0;
   return p;
 }
@@ -147,14 +157,18 @@ GemmPlan plan_prefill(int M, int N, int K) {
 
 // M <= 16: the built-in small-M path (or the override's); 16 < M <= 64: the
 // matrix-core GEMV unless the prefill kernel is forced; 64 < M <= 128: the
-// same GEMV in launches of 64 tokens (each streams the weights again: M=128
-// takes 2 x 12.5 us at N=14336, K=4096, where the prefill kernel's 56-112
-// tiles take 30-32 us); M > 128: prefill.
+// same GEMV in launches of 64 tokens (each streams the weights again), except
+// above 96 tokens when the prefill's 64-row tiles number >= 96, i.e. for
+// wide N (measured at N=14336, K=4096: two GEMV launches take 19.7 us at
+// M=96 and 22.2-22.9 us at M=104-128, the 112 prefill tiles 21.2 us; at
+// N=4096 the prefill would have 32 tiles); M > 128: prefill.
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   const int ovr = g_ovr_path.load();
   if (M > kChunkMaxM || (M > kLutMaxM && ovr == 1)) return plan_prefill(M, N, K);
-  if (M > kGemvMaxM) {   // two launches of the 64-token GEMV beat the few prefill tiles here
+  if (M > kGemvMaxM) {
+    const long long prefill_tiles = (long long)((M + 63) / 64) * ((N + 255) / 256);
+    if (ovr < 0 && M > kChunkPrefillM && prefill_tiles >= kPrefillMinTiles) return plan_prefill(M, N, K);
     GemmPlan c = plan_mfma_gemv(kGemvMaxM, N, K);
     c.chunk = kGemvMaxM;
     return c;

@@ -119,9 +119,12 @@ sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
  *   16 < M <= 64: the matrix-core GEMV with the tokens in two or four
  *            blocks of 16;
  *   64 < M <= 128: that GEMV in launches of 64 tokens on the same stream
- *            (sherry_workspace_bytes covers one launch);
- *   M > 128: the prefill GEMM (workgroup tiles of 128 tokens x 256 weight
- *            rows on the int8 matrix cores). */
+ *            (sherry_workspace_bytes covers one launch); above 96 tokens
+ *            the prefill GEMM instead when its 64-token tiles number at
+ *            least 96 (wide N);
+ *   M > 128: the prefill GEMM on the int8 matrix cores: workgroup tiles of
+ *            64 tokens x 256 weight rows when that grid fits the GPU in one
+ *            round (at most 256 tiles), else 128 tokens x 256 rows. */
 sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           const float* alpha, float* y, int64_t M, int64_t N,
                           int64_t K, void* workspace, size_t workspace_bytes,
@@ -218,12 +221,13 @@ sherry_status sherry_linear_plan(int64_t M, int64_t N, int64_t K, int* path,
  * built-in launch plan for shapes with M <= 128 for every later call in this
  * process (M > 128 always uses path 1):
  *   path   -1 = built-in choice, or 0, 1, 2 as in sherry_gemm_plan; for
- *          16 < M <= 128 only 1 changes the path (0 and 2 give path 2).
+ *          16 < M <= 128, 1 gives the prefill GEMM and 0 or 2 the GEMV.
  *   rw     path 0: row tiles per workgroup, 1, 2 or 4 (the workgroup's 4
  *          waves are rw row tiles x 4/rw waves sharing one);
  *          path 2: waves per workgroup sharing its one row tile, 4, 8 or
- *          16 (at most 8 when M > 16); 0 (or a value the path does not
- *          take) = built-in choice.
+ *          16 (at most 8 when M > 16);
+ *          path 1 (forced): 1 or 2 = tiles of 64 or 128 tokens;
+ *          0 (or a value the path does not take) = built-in choice.
  *   ch     path 0 only: k-tiles (128 inputs) per LDS table stage: 1, 2, 4
  *          or 8, capped so one stage stays within 32 KB; 0 = built-in.
  *   splits K-splits per output row group; 0 = built-in choice.

@@ -71,6 +71,40 @@ def test_plan_dispatch_rule():
     assert bw.workspace_bytes(512, 14336, 4096) == 0
 
 
+def test_prefill_tile_height_rule():
+    """The prefill GEMM takes tiles of 64 tokens when that grid fits the GPU
+    in one round (<= 256 tiles of 256 weight rows), else 128; above 96
+    tokens it replaces the 64-token GEMV launches when its 64-token tiles
+    number >= 96."""
+    lds64, lds128 = 78080, 107008      # the two kernels' LDS per workgroup
+    def tiles(M, N, bm):
+        return -(-M // bm) * -(-N // 256)
+    for M, N in [(129, 14336), (200, 14336), (256, 14336), (257, 14336), (512, 14336),
+                 (300, 4096), (1000, 4096), (1100, 4096), (129, 65536)]:
+        p = bw.plan(M, N, 4096)
+        assert p["path"] == "decode_mfma"
+        want64 = tiles(M, N, 64) <= 256
+        assert p["lds_bytes"] == (lds64 if want64 else lds128), (M, N)
+        nt = -(-N // 256)
+        assert p["grid"] == 8 * -(-nt // 8) * -(-M // (64 if want64 else 128)), (M, N)
+    # 96 < M <= 128: the prefill for wide N (>= 96 tiles of 64 tokens), else the GEMV launches
+    for M, N, want in [(96, 14336, "decode_mfma_gemv"), (97, 14336, "decode_mfma"),
+                       (128, 14336, "decode_mfma"), (128, 12288, "decode_mfma"),
+                       (128, 11008, "decode_mfma_gemv"), (100, 4096, "decode_mfma_gemv"),
+                       (65, 65536, "decode_mfma_gemv")]:
+        assert bw.plan(M, N, 4096)["path"] == want, (M, N)
+    try:   # forcing the GEMV keeps it there; forcing the prefill picks the height by rw
+        bw.plan_override("decode_mfma_gemv")
+        assert bw.plan(128, 14336, 4096)["path"] == "decode_mfma_gemv"
+        bw.plan_override("decode_mfma", 2)
+        assert bw.plan(100, 4096, 4096)["lds_bytes"] == lds128
+        bw.plan_override("decode_mfma", 1)
+        assert bw.plan(512, 14336, 4096)["lds_bytes"] == lds64
+        assert bw.plan(512, 14336, 4096)["grid"] == 8 * 7 * 8
+    finally:
+        bw.plan_override()
+
+
 def test_plan_override_changes_plan_and_workspace():
     try:
         base = bw.plan(1, 4096, 4096)

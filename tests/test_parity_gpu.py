@@ -179,16 +179,20 @@ def test_gemm_mfma_gemv_plans(orc, packed_cases, rw, splits, M, N, K):
     assert_y_close(gy.cpu().numpy(), y)
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64, 100, 128])
-def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M):
-    """The prefill kernel forced onto a small M (rows past M clamped)."""
+@pytest.mark.parametrize("bm", [1, 2])                 # tiles of 64 or 128 tokens
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64, 65, 100, 128, 129, 200, 300])
+def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M, bm):
+    """The prefill kernel forced onto small and mid M with either tile height
+    (rows past M clamped, a ragged last token tile)."""
     N, K = 320, 1152
     T, alpha, packed, galpha = packed_cases[(N, K)]
     q = synth.int8_uniform(M, K, seed=2900 + M)
     acc = orc.gemm_i32(q.numpy(), T)
     try:
-        bw.plan_override("decode_mfma")
-        assert bw.plan(M, N, K)["path"] == "decode_mfma"
+        bw.plan_override("decode_mfma", bm)
+        p = bw.plan(M, N, K)
+        assert p["path"] == "decode_mfma"
+        assert p["grid"] == 8 * 1 * -(-M // (64 * bm))   # 2 n tiles -> one per XCD slot
         gacc = bw.gemm_i32(q.cuda(), packed, N, K)
         torch.cuda.synchronize()
     finally:
@@ -263,12 +267,18 @@ def test_workload_parity(orc, name):
     _workload_check(orc, name)
 
 
-def test_workload_5_prefill_sampled(orc):
+@pytest.mark.parametrize("bm", [0, 1])    # built-in tiles (128 tokens here), or 64 forced
+def test_workload_5_prefill_sampled(orc, bm):
     w = synth.WORKLOADS["5"]
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N - 1],
                                      rng.choice(w.N, 251, replace=False)]))
-    _workload_check(orc, "5", sample_rows=rows)
+    try:
+        bw.plan_override("decode_mfma" if bm else None, bm)
+        _say(f"workload 5: {bw.plan(w.M, w.N, w.K)}")
+        _workload_check(orc, "5", sample_rows=rows)
+    finally:
+        bw.plan_override()
 
 
 # ------------------------------------------------------- HIP graph capture
@@ -620,7 +630,7 @@ def ragged_cases(orc):
 
 RAGGED_PLANS = [(None, 0, 0), ("decode_mfma_gemv", 4, 3), ("decode_mfma_gemv", 16, 1),
                 ("decode_mfma_gemv", 8, 2), ("lut_gemv", 0, 0), ("lut_gemv", 1, 3),
-                ("decode_mfma", 0, 0)]
+                ("decode_mfma", 0, 0), ("decode_mfma", 1, 0), ("decode_mfma", 2, 0)]
 
 
 @pytest.mark.parametrize("path,rw,splits,M", [
