@@ -21,7 +21,8 @@ quantization is fused into the product (as it is for this workload), else
 the product kernel the launch plan picks; "prefill" holds the M=512 decode + int8 MFMA
 product against the 5.0 POP/s int8 peak; "workloads" holds every workload's
 kernel time, and for M <= 16 the time of each small-M path (lookup-table
-GEMV and matrix-core GEMV); "grouped_qkv" and "grouped_gate_up" time three
+GEMV and matrix-core GEMV); "mid_m" times M = 16..200 tokens at the prefill
+layer's shape on the planned path; "grouped_qkv" and "grouped_gate_up" time three
 (two) projections of one x as one call on stacked packed weights against
 separate calls; "two_bit_baseline" times the
 same ternary weights in the plain 2-bit packing.  "cpu_baseline" times the
@@ -244,6 +245,30 @@ def two_bit_bench(torch, bw, synth, five_bit_us: dict):
     return res
 
 
+def mid_m_bench(torch, bw, synth, Ms=(16, 64, 128, 200)):
+    """The product between decode and prefill (chunked prefill) at the
+    prefill layer's shape, N=14336, K=4096 (workload 5's weights), on the
+    path the plan picks for each token count."""
+    w = synth.WORKLOADS["5"]
+    W = synth.workload_weights(w).cuda()
+    packed, alpha = bw.quantize_pack(W)
+    del W
+    R = copies_for(w.packed_bytes, 0)
+    packs = [packed] + [packed.clone() for _ in range(R - 1)]
+    out = {}
+    for M in Ms:
+        q = synth.int8_uniform(M, w.K, seed=4000 + M).cuda()
+        s = torch.ones(M, device="cuda")
+        y = torch.empty((M, w.N), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(max(bw.workspace_bytes(M, w.N, w.K), 256), dtype=torch.uint8, device="cuda")
+        ms, _ = graph_time(torch, lambda i: bw.gemm(q, s, packs[i % R], alpha, w.N, w.K, out=y, workspace=ws),
+                           max(100, R), reps=3)
+        out[str(M)] = {"plan": bw.plan(M, w.N, w.K), "us": round(ms * 1e3, 3),
+                       "TOPS": round(2 * M * w.N * w.K / ms / 1e9, 1),
+                       "packed_GB_s": round(w.packed_bytes / ms / 1e6, 1)}
+    return {"shape": f"M x (N={w.N}, K={w.K}), int8 x (sherry_gemm)", "rotating_copies": R, "M": out}
+
+
 def grouped_bench(torch, bw, synth, name: str = "2a", G: int = 3):
     """G projections of one token sharing x, as one sherry_linear call on the
     stacked packed weights versus G calls (rotating copies, as for the step):
@@ -442,6 +467,8 @@ def main():
                                        "traffic": traffic_from_profile(
                                            "mfma_gemm", "5", p5["plan"]),
                                        "kernel": "mfma_gemm_kernel"}}
+        out["mid_m"] = mid_m_bench(torch, bw, synth)
+        torch.cuda.empty_cache()
         out["grouped_qkv"] = grouped_bench(torch, bw, synth, "2a", 3)
         out["grouped_gate_up"] = grouped_bench(torch, bw, synth, "3a", 2)
         torch.cuda.empty_cache()
