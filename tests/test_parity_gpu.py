@@ -281,6 +281,48 @@ def test_workload_5_prefill_sampled(orc, bm):
         bw.plan_override()
 
 
+# ------------------------------------------------------ random shape sweep
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 129)), int(rng.integers(129, 201))]))
+        N = 4 * int(rng.integers(1, 257))          # 4 .. 1024, any multiple of 4
+        K = 16 * int(rng.integers(1, 129))         # 16 .. 2048, any multiple of 16
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(30, 9090))
+def test_random_shapes_every_path(orc, M, N, K):
+    """Seeded random shapes over the whole shape rule: the int32 product on
+    every path that takes the shape, and sherry_linear, against the oracle."""
+    W = synth.weights(N, K, 0.02, M % 3 == 0, seed=9100 + N + K)
+    x = synth.activations(M, K, seed=9200 + M + K, outlier_channels=(M % 2 == 0))
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    acc, y = orc.gemm(q, s, T, alpha)
+    packed, galpha = gpu_pack(W)
+    assert np.array_equal(packed.cpu().numpy(), orc.pack(T)), "packed codes"
+    gq, gs = bw.quantize_act(x.cuda())
+    paths = [(None, 0), ("decode_mfma", 1), ("decode_mfma", 2)]
+    if M <= 16:
+        paths += [("lut_gemv", 0), ("decode_mfma_gemv", 0)]
+    elif M <= 128:
+        paths += [("decode_mfma_gemv", 0)]
+    for path, rw in paths:
+        try:
+            bw.plan_override(path, rw)
+            _say(f"random M={M} N={N} K={K} path {path}/{rw}: {bw.plan(M, N, K)}")
+            gacc = bw.gemm_i32(gq, packed, N, K).cpu().numpy()
+        finally:
+            bw.plan_override()
+        assert np.array_equal(gacc, acc), f"acc ({path}, {rw})"
+    gy = bw.linear(x.cuda(), packed, galpha, N, K)
+    torch.cuda.synchronize()
+    assert_y_close(gy.cpu().numpy(), y)
+
+
 # ------------------------------------------------------- HIP graph capture
 @pytest.mark.parametrize("path,M,N,K", [(None, 1, 4096, 4096),        # fused step, K-split cells
                                         (None, 8, 1024, 2048),        # quantizer + GEMV
