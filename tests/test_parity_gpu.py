@@ -296,7 +296,8 @@ def _random_shapes(n, seed):
 @pytest.mark.parametrize("M,N,K", _random_shapes(30, 9090))
 def test_random_shapes_every_path(orc, M, N, K):
     """Seeded random shapes over the whole shape rule: the int32 product on
-    every path that takes the shape, and sherry_linear, against the oracle."""
+    every path that takes the shape, sherry_linear and (M <= 16) the 2-bit
+    product, against the oracle."""
     W = synth.weights(N, K, 0.02, M % 3 == 0, seed=9100 + N + K)
     x = synth.activations(M, K, seed=9200 + M + K, outlier_channels=(M % 2 == 0))
     T, alpha = orc.quantize(W.numpy())
@@ -321,6 +322,14 @@ def test_random_shapes_every_path(orc, M, N, K):
     gy = bw.linear(x.cuda(), packed, galpha, N, K)
     torch.cuda.synchronize()
     assert_y_close(gy.cpu().numpy(), y)
+    if M <= 16:                                    # the 2-bit format takes decode shapes
+        p2, a2 = bw.quantize_pack2(W.cuda())
+        gy2 = bw.gemm2(gq, gs, p2, a2, N, K)
+        gy5 = bw.gemm(gq, gs, packed, galpha, N, K)
+        torch.cuda.synchronize()
+        assert np.array_equal(p2.cpu().numpy(), orc.pack2(T)), "2-bit codes"
+        assert np.array_equal(gy2.cpu().numpy().view(np.uint32), gy5.cpu().numpy().view(np.uint32))
+        assert_y_close(gy2.cpu().numpy(), y)
 
 
 # ------------------------------------------------------- HIP graph capture
