@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import bit_weight_amd as bw
@@ -288,3 +289,53 @@ def test_two_bit_baseline_sizes_and_validation():
     assert need > 0
     assert g2(N=4096, K=4096, ws=None) == WS
     assert g2(N=4096, K=4096, wsb=need - 1) == WS
+
+
+def _random_shape_rule_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([rng.integers(1, 17), rng.integers(17, 129), rng.integers(129, 4097),
+                            rng.integers(1, 1 << 20)]))
+        N = 4 * int(rng.choice([rng.integers(1, 1025), rng.integers(1, 1 << 18)]))
+        K = 16 * int(rng.choice([rng.integers(1, 1025), rng.integers(1, 1 << 16)]))
+        out.append((M, N, K))
+    return out
+
+
+def test_plan_invariants_over_random_shapes():
+    """Host planning over 2000 seeded shapes of the whole shape rule: the path
+    rule, launch sizes that fit the hardware, K-splits that are all non-empty,
+    a workspace that holds one 64-bit cell per output of a launch whenever K
+    is split, and a fused sherry_linear only within its limits."""
+    for M, N, K in _random_shape_rule_shapes(2000, 4242):
+        p, lp = bw.plan(M, N, K), bw.linear_plan(M, N, K)
+        KT, RT = -(-K // 128), -(-N // 64)
+        assert p["block"] in (256, 512, 1024) and 1 <= p["grid"] < 2 ** 31, (M, N, K, p)
+        assert 0 < p["lds_bytes"] <= 160 * 1024, (M, N, K, p)
+        if M <= 16:
+            assert p["path"] in ("lut_gemv", "decode_mfma_gemv"), (M, N, K, p)
+        elif M <= 96:
+            assert p["path"] == "decode_mfma_gemv", (M, N, K, p)
+        elif M > 128:
+            assert p["path"] == "decode_mfma", (M, N, K, p)
+        ws = bw.workspace_bytes(M, N, K)
+        if p["path"] == "decode_mfma":
+            assert p["splits"] == 1 and ws == 0
+            bm = 64 if p["lds_bytes"] == 78080 else 128
+            assert p["lds_bytes"] in (78080, 107008)
+            assert p["grid"] == 8 * -(-(-(-N // 256)) // 8) * -(-M // bm), (M, N, K, p)
+            continue
+        s = p["splits"]
+        assert 1 <= s <= KT and -(-KT // -(-KT // s)) == s, (M, N, K, p)   # no empty split
+        if p["path"] == "lut_gemv":
+            assert p["grid"] % s == 0 and p["grid"] // s <= RT
+        else:
+            assert p["grid"] == RT * s, (M, N, K, p)
+        assert ws == (min(M, 64) * N * 8 if s > 1 else 0), (M, N, K, p, ws)
+        fused = lp["fused"]
+        assert fused == (bw.linear_scratch_bytes(M, N, K) == 0)
+        if fused:
+            assert M <= 4 and M * K <= 16384, (M, N, K, lp)
+            assert -(-KT // lp["splits"]) <= 32 and lp["block"] <= 1024
+            assert bw.workspace_bytes(M, N, K) >= (M * N * 8 if lp["splits"] > 1 else 0)
