@@ -194,7 +194,7 @@ sherry_status sherry_gemm2(const int8_t* x, const float* s_x, const void* packed
 /* Launch plan sherry_gemm uses for a shape (host-only, pure; for
  * diagnostics and benchmarks).  Any output pointer may be NULL.
  *   path: 0 = lookup-table GEMV (per-segment tables in LDS, §2.2; M <= 16),
- *         1 = decode + int8 matrix-core GEMM (the M > 128 path),
+ *         1 = decode + int8 matrix-core GEMM (M > 128, and M > 96 for wide N),
  *         2 = decode + int8 matrix-core GEMV (M <= 128; grid is per launch
  *             of at most 64 tokens).
  *   grid: workgroups per launch; block: threads per workgroup;
