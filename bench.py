@@ -306,8 +306,8 @@ def grouped_bench(torch, bw, synth, name: str = "2a", G: int = 3):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (got --gpus {args.gpus}); "
+              "sharding over several GPUs is described, not measured.", file=sys.stderr)
         sys.exit(2)
     import torch
     import bit_weight_amd as bw
