@@ -111,7 +111,7 @@ constexpr bool quad_x(int MT, int MB) { return MT == 16 && MB >= 1; }
 // (>= M*K / (4 * 64 * KW); the launch picks the smallest power of two).
 // SX = staged int8 activations: the split's x copied to LDS once, as in the
 // fused form, instead of loaded per k-tile (the launch uses it at M = 1).
-template <int KW, int MT, int MB, bool FQ, int FMT, int ST, int FS = 1, bool SX = false>
+template <int KW, int MT, int MB, bool FQ, int FMT, int ST, int FS = 1, bool SX = false, bool SL = false>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packed, const int8_t* x,
                                                             const float* xf, int M, int N, int K, int splits,
                                                             int kt_per_split, const float* s_x,
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
   lds_barrier();
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
 
-  auto step = [&](int i, v4u& w, v4u& h, v4u (&x0)[MB], v4u (&x1)[MB]) {
+  auto step = [&](int i, bool refill, v4u& w, v4u& h, v4u (&x0)[MB], v4u (&x1)[MB]) {
     uint32_t lo[kBlk], hi[kBlk];
     uint32_t f0[kBlk], f1[kBlk];
     if constexpr (FMT == 0) {
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
         }
       }
     }
-    load(i + kStages, w, h, x0, x1);
+    if (refill) load(i + kStages, w, h, x0, x1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
@@ -367,14 +367,30 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  int i = 0;
-  for (; i + kStages <= nk; i += kStages) {
+  if constexpr (SL) {
+    // at most 2 * kStages k-tiles per wave: straight-line steps, so no loop
+    // carries the in-flight stage registers around a back edge (there the
+    // compiler copies them into place, waiting for every load).  Past the
+    // wave's last k-tile only the arithmetic is skipped; the refills are
+    // issued regardless (re-reading its last tile), so no branch merges the
+    // stage registers.
 #pragma unroll
-    for (int st = 0; st < kStages; ++st) step(i + st, cw[st], ch[st], xa[st], xb[st]);
+    for (int i = 0; i < 2 * kStages; ++i) {
+      const int st = i % kStages;
+      if (i < nk) step(i, false, cw[st], ch[st], xa[st], xb[st]);
+      if (i + kStages < 2 * kStages) load(i + kStages, cw[st], ch[st], xa[st], xb[st]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    int i = 0;
+    for (; i + kStages <= nk; i += kStages) {
+#pragma unroll
+      for (int st = 0; st < kStages; ++st) step(i + st, true, cw[st], ch[st], xa[st], xb[st]);
+    }
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st)
+      if (i + st < nk) step(i + st, true, cw[st], ch[st], xa[st], xb[st]);
   }
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (i + st < nk) step(i + st, cw[st], ch[st], xa[st], xb[st]);
 
   // Epilogue, one token block at a time.  Every wave writes its sums to LDS
   // as [token][row]; then each lane owns one weight row and a fixed set of
@@ -468,20 +484,38 @@ hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     // one token: its split's int8 x staged in LDS (measured 2-4 % faster at
     // M=1; at M=4 the chunk loads, sized for the longest split, cost more
     // than the per-step loads they replace)
-    if (a.M <= 1 && p.kt_per_split <= kFuseMaxSpan)
-      launch_product_kernel(mfma_gemv_kernel<KW, 1, 1, false, FMT, 4, 1, true>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 1) launch_product_kernel(mfma_gemv_kernel<KW, 1, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 2) launch_product_kernel(mfma_gemv_kernel<KW, 2, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 4) launch_product_kernel(mfma_gemv_kernel<KW, 4, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 8) launch_product_kernel(mfma_gemv_kernel<KW, 8, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if (a.M <= 16) launch_product_kernel(mfma_gemv_kernel<KW, 16, 1, false, FMT, 4>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-    else if constexpr (FMT == 0 && KW <= 8) {   // 16 waves leave too few registers for two blocks
-      if (a.M <= 32) launch_product_kernel(mfma_gemv_kernel<KW, 16, 2, false, 0, 3>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-      else if (a.M <= kGemvMaxM) launch_product_kernel(mfma_gemv_kernel<KW, 16, 4, false, 0, 2>, grid, block, 0, stream, a, p.splits, p.kt_per_split);
-      else return hipErrorInvalidValue;
+    // straight-line steps for one token block with no K-split and 4 to 8
+    // k-tiles per wave (measured at M=8, K=8192, N=28672: 13.4 -> 12.2 us;
+    // with fewer k-tiles the loop never takes its back edge, and with
+    // several token blocks it was 2 % slower)
+    const int nkw = (p.kt_per_split + KW - 1) / KW;
+    const bool sl4 = p.splits == 1 && nkw >= 4 && nkw <= 8;
+#define SHERRY_GEMV(MT_, MB_, ST_, SX_, SL_) \
+  launch_product_kernel(mfma_gemv_kernel<KW, MT_, MB_, false, FMT, ST_, 1, SX_, SL_>, grid, block, 0, stream, a, p.splits, p.kt_per_split)
+    if (a.M <= 1 && p.kt_per_split <= kFuseMaxSpan) {
+      if (sl4) SHERRY_GEMV(1, 1, 4, true, true); else SHERRY_GEMV(1, 1, 4, true, false);
+    } else if (a.M <= 1) {
+      if (sl4) SHERRY_GEMV(1, 1, 4, false, true); else SHERRY_GEMV(1, 1, 4, false, false);
+    } else if (a.M <= 2) {
+      if (sl4) SHERRY_GEMV(2, 1, 4, false, true); else SHERRY_GEMV(2, 1, 4, false, false);
+    } else if (a.M <= 4) {
+      if (sl4) SHERRY_GEMV(4, 1, 4, false, true); else SHERRY_GEMV(4, 1, 4, false, false);
+    } else if (a.M <= 8) {
+      if (sl4) SHERRY_GEMV(8, 1, 4, false, true); else SHERRY_GEMV(8, 1, 4, false, false);
+    } else if (a.M <= 16) {
+      if (sl4) SHERRY_GEMV(16, 1, 4, false, true); else SHERRY_GEMV(16, 1, 4, false, false);
+    } else if constexpr (FMT == 0 && KW <= 8) {   // 16 waves leave too few registers for two blocks
+      if (a.M <= 32) {
+        SHERRY_GEMV(16, 2, 3, false, false);
+      } else if (a.M <= kGemvMaxM) {
+        SHERRY_GEMV(16, 4, 2, false, false);
+      } else {
+        return hipErrorInvalidValue;
+      }
     } else {
       return hipErrorInvalidValue;
     }
+#undef SHERRY_GEMV
     return hipGetLastError();
   }
 }

@@ -179,6 +179,41 @@ def test_gemm_mfma_gemv_plans(orc, packed_cases, rw, splits, M, N, K):
     assert_y_close(gy.cpu().numpy(), y)
 
 
+# (waves per row tile, K): 4 to 8 k-tiles per wave with no K-split, which the
+# GEMV runs as straight-line steps; ragged k-tile counts leave the waves
+# uneven, and K = 1584 and 7248 end in a ragged k-tile
+STRAIGHT_LINE = [(4, 13 * 128), (4, 1584), (4, 32 * 128), (8, 57 * 128), (8, 7248), (16, 128 * 128)]
+
+
+@pytest.mark.parametrize("rw,K", STRAIGHT_LINE)
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+def test_gemm_gemv_straight_line_steps(orc, rw, K, M):
+    """The GEMV's straight-line form (no K-split, 4 to 8 k-tiles per wave),
+    with one token staged in LDS or loaded per step, on both code formats."""
+    N = 192
+    W = synth.weights(N, K, 0.02, M % 2 == 1, seed=7100 + K + rw)
+    T, alpha = orc.quantize(W.numpy())
+    packed, galpha = gpu_pack(W)
+    p2, a2 = bw.quantize_pack2(W.cuda())
+    q = synth.int8_uniform(M, K, seed=7200 + M + K)
+    s_x = (torch.rand(M, generator=torch.Generator().manual_seed(M + 11)) * 0.05 + 0.001).float()
+    acc, y = orc.gemm(q.numpy(), s_x.numpy(), T, alpha)
+    try:
+        bw.plan_override("decode_mfma_gemv", rw, 0, 1)
+        p = bw.plan(M, N, K)
+        _say(f"straight-line gemv rw={rw} M={M} N={N} K={K}: {p}")
+        assert p["splits"] == 1 and 4 <= -(-((K + 127) // 128) // rw) <= 8
+        gacc = bw.gemm_i32(q.cuda(), packed, N, K)
+        gy = bw.gemm(q.cuda(), s_x.cuda(), packed, galpha, N, K)
+        gy2 = bw.gemm2(q.cuda(), s_x.cuda(), p2, a2, N, K)
+        torch.cuda.synchronize()
+    finally:
+        bw.plan_override()
+    assert np.array_equal(gacc.cpu().numpy(), acc)
+    assert_y_close(gy.cpu().numpy(), y)
+    assert np.array_equal(gy2.cpu().numpy().view(np.uint32), gy.cpu().numpy().view(np.uint32))
+
+
 @pytest.mark.parametrize("bm", [1, 2])                 # tiles of 64 or 128 tokens
 @pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64, 65, 100, 128, 129, 200, 300])
 def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M, bm):
