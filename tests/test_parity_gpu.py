@@ -214,6 +214,36 @@ def test_gemm_gemv_straight_line_steps(orc, rw, K, M):
     assert np.array_equal(gy2.cpu().numpy().view(np.uint32), gy.cpu().numpy().view(np.uint32))
 
 
+# (the fused form holds at most 32 k-tiles: 8 waves reach 4 k-tiles from 25 on)
+@pytest.mark.parametrize("rw,K,M", [(4, 13 * 128, 4), (4, 1584, 3), (4, 32 * 128, 1), (4, 32 * 128, 4),
+                                    (8, 29 * 128, 2), (8, 3952, 1)])
+def test_linear_fused_unsplit_long_waves(orc, rw, K, M):
+    """sherry_linear's fused form (quantization inside the product) with no
+    K-split and 4 to 8 k-tiles per wave, the range where the unfused product
+    takes straight-line steps (the fused kernel keeps its loop): y matches
+    the oracle and is bit-identical to sherry_quantize_act + sherry_gemm."""
+    N = 192
+    W = synth.weights(N, K, 0.02, True, seed=7300 + K + rw)
+    x = synth.activations(M, K, seed=7400 + M + K, outlier_channels=True)
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    _, y = orc.gemm(q, s, T, alpha)
+    packed, galpha = gpu_pack(W)
+    try:
+        bw.plan_override("decode_mfma_gemv", rw, 0, 1)
+        lp = bw.linear_plan(M, N, K)
+        _say(f"fused unsplit rw={rw} M={M} N={N} K={K}: {lp}")
+        assert lp["fused"] and lp["splits"] == 1
+        gl = bw.linear(x.cuda(), packed, galpha, N, K)
+        gq, gs = bw.quantize_act(x.cuda())
+        gy = bw.gemm(gq, gs, packed, galpha, N, K)
+        torch.cuda.synchronize()
+    finally:
+        bw.plan_override()
+    assert np.array_equal(gl.cpu().numpy().view(np.uint32), gy.cpu().numpy().view(np.uint32))
+    assert_y_close(gl.cpu().numpy(), y)
+
+
 @pytest.mark.parametrize("bm", [1, 2])                 # tiles of 64 or 128 tokens
 @pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64, 65, 100, 128, 129, 200, 300])
 def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M, bm):
