@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_HERE, "libsherry.so")
 STATUS = {
     0: "SHERRY_OK", -1: "SHERRY_ERR_NULL", -2: "SHERRY_ERR_SHAPE",
     -3: "SHERRY_ERR_ALIGN", -4: "SHERRY_ERR_WORKSPACE", -5: "SHERRY_ERR_HIP",
-    -6: "SHERRY_ERR_DEVICE",
+    -6: "SHERRY_ERR_DEVICE", -7: "SHERRY_ERR_PARTIAL",
 }
 
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
                 "sherry_gemm2_workspace_bytes": ([i64, i64, i64], sz),
                 "sherry_gemm2": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
                 "sherry_linear": ([vp, vp, vp, vp, i64, i64, i64, vp, sz, vp, sz, vp], ci),
+                "sherry_probe_read": ([vp, sz, vp, ci, ci, ci, vp], ci),
+                "sherry_probe_empty": ([vp], ci),
             }
             for name, (args, res) in sigs.items():
                 fn = getattr(L, name)
@@ -250,6 +252,22 @@ def gemm_i32(x: torch.Tensor, packed: torch.Tensor, N: int, K: int,
     _check(lib().sherry_gemm_i32(px, packed.data_ptr(), pa, M, N, K, wp, wn, _stream(x.device)),
            "sherry_gemm_i32")
     return out
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, grid: int, block: int, unroll: int) -> None:
+    """Diagnostic: stream-read all of `buf` (a contiguous device tensor whose
+    byte size is a multiple of 16); `sink` is a device int32 tensor."""
+    if not buf.is_contiguous() or buf.device.type != "cuda":
+        raise RuntimeError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().sherry_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, block, unroll,
+                                   _stream(buf.device)), "sherry_probe_read")
+
+
+def probe_empty(device=None) -> None:
+    """Diagnostic: one empty kernel launch on the current stream."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    _check(lib().sherry_probe_empty(_stream(dev)), "sherry_probe_empty")
 
 
 def linear_scratch_bytes(M: int, N: int, K: int) -> int:

@@ -19,7 +19,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsherry.so")
-SOURCES = ["sherry_abi.hip", "pack.hip", "lut_gemv.hip", "mfma_gemm.hip", "mfma_gemv.hip"]
+SOURCES = ["sherry_abi.hip", "pack.hip", "lut_gemv.hip", "mfma_gemm.hip", "mfma_gemv.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

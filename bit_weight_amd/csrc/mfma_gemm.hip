@@ -214,8 +214,11 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   for (int i = tid; i < 1024; i += kThreads)
     dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
 
-  // This wave's row tile (N % 64 == 0, so a row tile is all valid or all
-  // past N; one past N streams the last tile and stores nothing).
+  // This wave's row tile.  One wholly past N (N not a multiple of 256)
+  // streams the last row tile again and stores nothing.  In a ragged last
+  // row tile (N % 64 != 0) the padding rows decode code 0, the block
+  // (0,+1,+1,+1), and form sums of their own: only the n < N mask of the
+  // epilogue's stores keeps them out of the output.
   const int rt_raw = n0 / kTileRows + wave;
   const bool n_live = rt_raw < RT;
   const int rt = n_live ? rt_raw : RT - 1;

@@ -108,7 +108,9 @@ void set_plan_override(int path, int rw, int ch, int splits) {
   g_ovr_splits = splits;
 }
 
-hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream) {
+hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream,
+                          bool* partial) {
+  if (partial) *partial = false;
   auto one = [&](const GemmArgs& a) {
     return plan.path == 0   ? launch_lut_gemv(plan, a, stream)
            : plan.path == 2 ? launch_mfma_gemv(plan, a, stream)
@@ -116,7 +118,9 @@ hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_
   };
   if (plan.chunk <= 0 || args.M <= plan.chunk) return one(args);
   // launches of plan.chunk tokens in stream order; each leaves the split-K
-  // workspace zero for the next
+  // workspace zero for the next.  A launch that fails to enqueue runs
+  // nothing, so the workspace stays zero, but the tokens of the launches
+  // before it are written and the later ones are not: *partial says so.
   for (int m0 = 0; m0 < args.M; m0 += plan.chunk) {
     GemmArgs c = args;
     c.M = args.M - m0 < plan.chunk ? args.M - m0 : plan.chunk;
@@ -125,7 +129,10 @@ hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_
     if (args.y) c.y = args.y + (size_t)m0 * args.N;
     if (args.acc) c.acc = args.acc + (size_t)m0 * args.N;
     const hipError_t e = one(c);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+      if (partial) *partial = m0 > 0;
+      return e;
+    }
   }
   return hipSuccess;
 }
@@ -223,7 +230,7 @@ sherry_status run_gemm(const int8_t* x, const float* s_x, const void* packed, co
                        size_t workspace_bytes, void* stream) {
   if (!x || !packed || (y && (!s_x || !alpha)) || (!y && !acc)) return SHERRY_ERR_NULL;
   if (!shape_ok(M, N, K)) return SHERRY_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(packed, 16) || (y && !aligned(y, 4)) || (acc && !aligned(acc, 4)) ||
+  if (!aligned(x, 16) || !aligned(packed, 16) || (y && !aligned(y, 16)) || (acc && !aligned(acc, 16)) ||
       (s_x && !aligned(s_x, 4)) || (alpha && !aligned(alpha, 4)))
     return SHERRY_ERR_ALIGN;
   const GemmPlan plan = plan_gemm((int)M, (int)N, (int)K);
@@ -246,11 +253,14 @@ sherry_status run_gemm(const int8_t* x, const float* s_x, const void* packed, co
   args.K = (int)K;
   if (plan.ws_bytes > 0) args.partials = static_cast<int32_t*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = launch_product(plan, args, s);
-  return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+  bool partial = false;
+  const hipError_t e = launch_product(plan, args, s, &partial);
+  return e == hipSuccess ? SHERRY_OK : (partial ? SHERRY_ERR_PARTIAL : SHERRY_ERR_HIP);
 }
 
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+
 
 // Scratch of sherry_linear: q [M,K] and s_x [M] when the quantization is
 // not fused into the product (any content; not kept zero).
@@ -295,6 +305,9 @@ const char* sherry_status_string(int status) {
     case SHERRY_ERR_WORKSPACE: return "SHERRY_ERR_WORKSPACE: workspace missing or too small";
     case SHERRY_ERR_HIP: return "SHERRY_ERR_HIP: a HIP call or kernel launch failed";
     case SHERRY_ERR_DEVICE: return "SHERRY_ERR_DEVICE: current device is not gfx950";
+    case SHERRY_ERR_PARTIAL:
+      return "SHERRY_ERR_PARTIAL: a launch failed after earlier launches of the call were enqueued; "
+             "the output is incomplete, the workspace is left zero";
     default: return "SHERRY_ERR_UNKNOWN";
   }
 }
@@ -408,7 +421,7 @@ sherry_status sherry_gemm2(const int8_t* x, const float* s_x, const void* packed
                            size_t workspace_bytes, void* stream) {
   if (!x || !s_x || !packed || !alpha || !y) return SHERRY_ERR_NULL;
   if (!shape_ok(M, N, K) || M > kLutMaxM) return SHERRY_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 4) || !aligned(s_x, 4) ||
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || !aligned(s_x, 4) ||
       !aligned(alpha, 4))
     return SHERRY_ERR_ALIGN;
   const GemmPlan plan = plan_mfma_gemv((int)M, (int)N, (int)K);
@@ -443,7 +456,7 @@ sherry_status sherry_linear(const float* x, const void* packed, const float* alp
                             void* stream) {
   if (!x || !packed || !alpha || !y) return SHERRY_ERR_NULL;
   if (!shape_ok(M, N, K)) return SHERRY_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(alpha, 4) || !aligned(y, 4))
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(alpha, 4) || !aligned(y, 16))
     return SHERRY_ERR_ALIGN;
   GemmPlan plan;
   bool fused = false;
@@ -468,6 +481,7 @@ sherry_status sherry_linear(const float* x, const void* packed, const float* alp
   args.K = (int)K;
   if (plan.ws_bytes > 0) args.partials = static_cast<int32_t*>(workspace);
   hipError_t e;
+  bool partial = false;
   if (fused) {
     args.xf = x;
     e = plan.path == 0 ? launch_lut_gemv(plan, args, st) : launch_mfma_gemv(plan, args, st);
@@ -478,10 +492,11 @@ sherry_status sherry_linear(const float* x, const void* packed, const float* alp
     if (e == hipSuccess) {
       args.x = q;
       args.s_x = s_x;
-      e = launch_product(plan, args, st);
+      e = launch_product(plan, args, st, &partial);
+      partial = true;   // the quantizer's launch was enqueued before it
     }
   }
-  return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+  return e == hipSuccess ? SHERRY_OK : (partial ? SHERRY_ERR_PARTIAL : SHERRY_ERR_HIP);
 }
 
 }  // extern "C"

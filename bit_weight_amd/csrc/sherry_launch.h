@@ -105,7 +105,9 @@ int mfma_gemm_lds_bytes(int bm);
 int mfma_gemm_threads();
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 // The product (x int8) on the plan's path, in launches of plan.chunk tokens
-// when the plan asks for it.
-hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
+// when the plan asks for it.  On a failed launch, *partial (if given) tells
+// whether earlier launches of the same call were already enqueued.
+hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream,
+                          bool* partial = nullptr);
 
 }  // namespace sherry

@@ -26,8 +26,10 @@
  *     visible after the caller synchronizes the stream.
  *   - Argument errors are found on the host before any HIP call; such a call
  *     enqueues nothing and returns a negative status.  A failed launch
- *     returns SHERRY_ERR_HIP.  A fault inside a kernel is reported by the
- *     caller's next synchronizing HIP call, not by this library.
+ *     returns SHERRY_ERR_HIP, or SHERRY_ERR_PARTIAL when launches of the
+ *     same call were enqueued before it.  A fault inside a kernel is
+ *     reported by the caller's next synchronizing HIP call, not by this
+ *     library.
  *   - Shapes supported: K % 16 == 0, N % 4 == 0, 1 <= M,N,K <= 2^20
  *     (whole 4-weight blocks, 16-byte aligned int8 activation rows and
  *     whole 16-byte output stores).
@@ -60,7 +62,15 @@ typedef enum {
   SHERRY_ERR_ALIGN = -3,     /* a pointer is not aligned as required */
   SHERRY_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
   SHERRY_ERR_HIP = -5,       /* a HIP runtime call or launch failed */
-  SHERRY_ERR_DEVICE = -6     /* the current device is not a gfx950 GPU */
+  SHERRY_ERR_DEVICE = -6,    /* the current device is not a gfx950 GPU */
+  SHERRY_ERR_PARTIAL = -7    /* a launch failed after earlier launches of the
+                                same call were enqueued (sherry_linear's
+                                quantizer, or the 64-token launches of
+                                64 < M <= 128): those complete, so the output
+                                is partly written; a launch that fails runs
+                                nothing and every launch that runs leaves the
+                                split-K workspace zero, so the workspace needs
+                                no re-zeroing */
 } sherry_status;
 
 /* Human-readable name of a status code (static string; never NULL). */
@@ -105,7 +115,9 @@ sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
  *   x        [M,K] int8, 16-byte aligned.
  *   s_x      [M] fp32.            alpha  [N] fp32 (from sherry_quantize_pack).
  *   packed   packed weights, 16-byte aligned.
- *   y        [M,N] fp32 (written), 4-byte aligned.
+ *   y        [M,N] fp32 (written), 16-byte aligned (with N % 4 == 0 every
+ *            row then starts on a 16-byte boundary; the prefill GEMM stores
+ *            16 bytes per lane).
  *   workspace / workspace_bytes: scratch of at least
  *            sherry_workspace_bytes(M,N,K) bytes, 256-byte aligned, zero
  *            filled before first use (may be NULL when that size is 0).
@@ -131,7 +143,7 @@ sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           void* stream);
 
 /* Same product, stopping at the int32 accumulators: acc [M,N] int32
- * (written, 4-byte aligned).  Same kernels and workspace rules. */
+ * (written, 16-byte aligned).  Same kernels and workspace rules. */
 sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,
                               int64_t M, int64_t N, int64_t K, void* workspace,
                               size_t workspace_bytes, void* stream);
@@ -235,6 +247,23 @@ sherry_status sherry_linear_plan(int64_t M, int64_t N, int64_t K, int* path,
  * override, so query it after setting one.  Not thread-safe with respect to
  * concurrent calls.  Returns SHERRY_ERR_SHAPE for an invalid value. */
 sherry_status sherry_gemm_plan_override(int path, int rw, int ch, int splits);
+
+/* --- Diagnostics (not part of the product) -------------------------------
+ * Ceilings for the benchmark, measured in the same process as the product:
+ * the plain streaming-read rate of a device buffer and the cost of an empty
+ * launch. */
+
+/* Reads `bytes` (a multiple of 16) of device memory at `src` (16-byte
+ * aligned) with 16-byte loads: grid x block threads (block a multiple of 64,
+ * at most 1024), each keeping `unroll` (1, 2, 4 or 8) loads in flight, the
+ * grid walking the buffer front to back.  Nothing is written unless the XOR
+ * of all the data equals one fixed constant; then one dword goes to `sink`
+ * (device, 4-byte aligned).  Asynchronous on `stream`. */
+sherry_status sherry_probe_read(const void* src, size_t bytes, void* sink, int grid, int block,
+                                int unroll, void* stream);
+
+/* Enqueues an empty kernel (one workgroup of 64 threads) on `stream`. */
+sherry_status sherry_probe_empty(void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,27 +22,38 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sherry_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# the same source built with OpenMP: only the int32 product runs on several
+# threads (its outputs are independent sums, so the values are identical)
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
 CXXFLAGS = ["-std=c++17", "-O2", "-fno-fast-math", "-ffp-contract=off",
             "-shared", "-fPIC"]
+OMP_FLAGS = ["-fopenmp"]
 
-_lib = None
+_libs = {}
+
+
+def _compile(out: str, extra) -> None:
+    tmp = out + ".tmp"
+    subprocess.check_call(["g++", *CXXFLAGS, *extra, _SRC, "-o", tmp])
+    os.replace(tmp, out)
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle into ``oracle/liboracle.so`` with g++."""
+    """Compile the oracle into ``oracle/liboracle.so`` (single-threaded) and
+    ``oracle/liboracle_omp.so`` (the same source with OpenMP) with g++."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["g++", *CXXFLAGS, _SRC, "-o", tmp])
-        os.replace(tmp, _LIB)
+        _compile(_LIB, [])
+    if force or not os.path.exists(_LIB_OMP):
+        _compile(_LIB_OMP, OMP_FLAGS)
     return _LIB
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB)
+def _load(parallel: bool = False):
+    path = _LIB_OMP if parallel else _LIB
+    if path not in _libs:
+        if not os.path.exists(path):
+            _compile(path, OMP_FLAGS if parallel else [])
+        lib = ctypes.CDLL(path)
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         sigs = {
             "oracle_pattern": [ci, vp],
@@ -59,13 +70,19 @@ def _load():
             "oracle_lut": [vp, i64, i64, vp],
             "oracle_gemm_i32": [vp, vp, i64, i64, i64, vp],
             "oracle_epilogue": [vp, vp, vp, i64, i64, vp],
+            "oracle_threads": [],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = i64 if name.endswith("_bytes") else ci
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]
+
+
+def threads(parallel: bool = True) -> int:
+    """Threads the int32 product uses in the plain (1) or OpenMP build."""
+    return int(_load(parallel).oracle_threads())
 
 
 def _p(a: np.ndarray):
@@ -173,15 +190,17 @@ def lut(q: np.ndarray) -> np.ndarray:
     return L
 
 
-def gemm_i32(q: np.ndarray, T: np.ndarray) -> np.ndarray:
-    """acc[m,n] = sum_k q[m,k] * T[n,k] (plain triple loop, int64 -> int32)."""
+def gemm_i32(q: np.ndarray, T: np.ndarray, parallel: bool = False) -> np.ndarray:
+    """acc[m,n] = sum_k q[m,k] * T[n,k] (plain triple loop, int64 -> int32).
+    parallel=True runs the same source's OpenMP build (weight rows spread over
+    the host cores; identical values)."""
     q = np.ascontiguousarray(q, dtype=np.int8)
     T = np.ascontiguousarray(T, dtype=np.int8)
     M, K = q.shape
     N, K2 = T.shape
     assert K == K2
     acc = np.empty((M, N), np.int32)
-    _check(_load().oracle_gemm_i32(_p(q), _p(T), M, N, K, _p(acc)), "gemm_i32")
+    _check(_load(parallel).oracle_gemm_i32(_p(q), _p(T), M, N, K, _p(acc)), "gemm_i32")
     return acc
 
 
@@ -197,7 +216,7 @@ def epilogue(acc: np.ndarray, s_x: np.ndarray, alpha: np.ndarray) -> np.ndarray:
     return y
 
 
-def gemm(q, s_x, T, alpha):
+def gemm(q, s_x, T, alpha, parallel: bool = False):
     """Full product: int32 accumulators and the fp32 output."""
-    acc = gemm_i32(q, T)
+    acc = gemm_i32(q, T, parallel)
     return acc, epilogue(acc, s_x, alpha)

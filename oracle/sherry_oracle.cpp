@@ -42,11 +42,17 @@
 // uses them).  Total Np*Kp*5/32 bytes.
 //
 // Build: g++ -std=c++17 -O2 -fno-fast-math -ffp-contract=off -shared -fPIC
+// (liboracle.so, single-threaded).  The same source built with -fopenmp
+// (liboracle_omp.so) runs the int32 product over all host cores; nothing
+// else differs.
 
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 namespace {
 
@@ -323,20 +329,35 @@ int oracle_lut(const int8_t* q, int64_t M, int64_t K, int32_t* L) {
 }
 
 // acc[m,n] = sum_k q[m,k] * T[n,k]: the dense int8 x unpacked-ternary product.
-// Returns -2 if any result would not fit int32.
+// Returns -2 if any result would not fit int32.  Every output is its own
+// plain sum; the outputs are independent, so the build with OpenMP
+// (liboracle_omp.so, the same source) only spreads the weight rows over
+// threads and returns identical values.
 int oracle_gemm_i32(const int8_t* q, const int8_t* T, int64_t M, int64_t N,
                     int64_t K, int32_t* acc) {
   if (M <= 0 || N <= 0 || K <= 0) return -1;
-  for (int64_t m = 0; m < M; ++m)
-    for (int64_t n = 0; n < N; ++n) {
+  int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t m = 0; m < M; ++m) {
       int64_t a = 0;
       const int8_t* qr = q + m * K;
       const int8_t* tr = T + n * K;
       for (int64_t k = 0; k < K; ++k) a += (int64_t)qr[k] * (int64_t)tr[k];
-      if (a > INT32_MAX || a < INT32_MIN) return -2;
-      acc[m * N + n] = (int32_t)a;
+      if (a > INT32_MAX || a < INT32_MIN) overflow = 1;
+      else acc[m * N + n] = (int32_t)a;
     }
-  return 0;
+  return overflow ? -2 : 0;
+}
+
+// Threads the product above runs on: 1 in the plain build, the OpenMP
+// team size in the OpenMP build.
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 // [Sherry §2.2, step 4] y = ((float)acc * s_x[m]) * alpha[n].

@@ -37,6 +37,10 @@ def test_status_strings():
     for code, name in bw.STATUS.items():
         assert L.sherry_status_string(code).decode().startswith(name)
     assert L.sherry_status_string(99).decode() == "SHERRY_ERR_UNKNOWN"
+    # every status the header declares has a name in the binding
+    declared = {int(v): k for k, v in re.findall(r"\b(SHERRY_\w+)\s*=\s*(-?\d+)", open(HEADER).read())}
+    assert declared == bw.STATUS
+    assert "workspace is left zero" in L.sherry_status_string(-7).decode()
 
 
 def test_packed_bytes():
@@ -168,6 +172,9 @@ def test_gemm_misaligned():
     assert _gemm(x=FAKE + 4) == ALIGN
     assert _gemm(p=FAKE + 8) == ALIGN
     assert _gemm(y=FAKE + 2) == ALIGN
+    # outputs are 16-byte aligned (the prefill GEMM stores 16 bytes per lane)
+    assert _gemm(y=FAKE + 4) == ALIGN
+    assert _gemm(y=FAKE + 8) == ALIGN
     assert _gemm(s=FAKE + 1) == ALIGN
     assert _gemm(al=FAKE + 2) == ALIGN
 

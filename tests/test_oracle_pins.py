@@ -319,3 +319,98 @@ def test_padded_layout_is_code_zero_padding(orc, N, K):
     full2[:N, :K] = T
     assert np.array_equal(orc.pack2(T), orc.pack2(full2))
     assert np.array_equal(orc.unpack2(orc.pack2(T), N, K), T)
+
+
+# ------------------------------------------- scaled act quant, epilogue order
+# Golden values written by tests/golden/make_*.py with exact rational
+# arithmetic (fractions.Fraction): no oracle and no GPU took part.
+import sys as _sys  # noqa: E402
+
+_sys.path.insert(0, GOLDEN)
+import exact_fp32  # noqa: E402
+import make_act_quant_scaled  # noqa: E402
+import make_epilogue_order  # noqa: E402
+
+
+def _act_quant_scaled_rows():
+    rows, cur = [], {}
+    with open(os.path.join(GOLDEN, "act_quant_scaled.txt")) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            key, val = line.split(":", 1)
+            cur[key.strip()] = val.split()
+            if key.strip() == "q":
+                rows.append((np.array([exact_fp32.from_hex(v) for v in cur["x"]], np.float32),
+                             exact_fp32.from_hex(cur["s"][0]),
+                             np.array([int(v) for v in cur["q"]], np.int8)))
+                cur = {}
+    return rows
+
+
+def test_golden_files_are_what_their_scripts_write():
+    for name, mod in (("act_quant_scaled.txt", make_act_quant_scaled),
+                      ("epilogue_order.txt", make_epilogue_order)):
+        with open(os.path.join(GOLDEN, name)) as f:
+            assert f.read() == mod.render(), f"{name} differs from its writer's output"
+
+
+def test_exact_fp32_rounding_agrees_with_ieee_on_known_values():
+    # the helpers themselves: 1/3 and 2/3 in binary32, a tie, and a power of two
+    F = exact_fp32.Fraction
+    assert float(exact_fp32.fp32_round(F(1, 3))) == float(np.float32(1) / np.float32(3))
+    assert float(exact_fp32.fp32_round(F(2, 3))) == float(np.float32(2) / np.float32(3))
+    # 1 + 2^-24 lies halfway between 1 and 1 + 2^-23: ties to the even significand (1)
+    assert exact_fp32.fp32_round(1 + F(1, 2 ** 24)) == 1
+    assert exact_fp32.fp32_round(1 + F(3, 2 ** 24)) == 1 + F(2, 2 ** 23)
+    assert exact_fp32.fp32_round(F(2) ** -100) == F(2) ** -100
+    assert [exact_fp32.round_half_even(F(v, 2)) for v in (-5, -3, -1, 1, 3, 5)] == [-2, -2, 0, 0, 2, 2]
+
+
+def test_act_quant_golden_scaled(orc):
+    """Scales other than 1: q follows one correctly rounded fp32 division x/s
+    and a round-half-even of that fp32 quotient (the workloads' rule s =
+    max|x|/127, symmetric; reading of the quantizer)."""
+    rows = _act_quant_scaled_rows()
+    assert len(rows) == 3
+    X = np.stack([r[0] for r in rows])
+    q, s = orc.act_quant(X)
+    for m, (x, s_ref, q_ref) in enumerate(rows):
+        assert s[m].view(np.uint32) == np.float32(s_ref).view(np.uint32)
+        assert np.array_equal(q[m], q_ref), f"token {m}"
+        # the golden separates the reading from its two near alternatives
+        rcp = np.clip(np.rint(x * (np.float32(1) / np.float32(s_ref))), -127, 127)
+        exact = np.clip(np.rint(x.astype(np.float64) / np.float64(s_ref)), -127, 127)
+        assert (rcp != q_ref).any() and (exact != q_ref).any()
+
+
+def _epilogue_cases():
+    out = []
+    with open(os.path.join(GOLDEN, "epilogue_order.txt")) as f:
+        for line in f:
+            if line.startswith("case:"):
+                a, s, al, y = line.split(":", 1)[1].split()
+                out.append((int(a), exact_fp32.from_hex(s), exact_fp32.from_hex(al),
+                            exact_fp32.from_hex(y)))
+    return out
+
+
+def test_epilogue_order_golden(orc):
+    """y = ((float)acc * s_x) * alpha, each product rounded to fp32 in that
+    order (the page's single float rescale after the integer add tree; reading
+    of the epilogue).  Every case is one where the other two orders differ."""
+    cases = _epilogue_cases()
+    assert len(cases) == 48
+    for acc, s, al, y_ref in cases:
+        y = orc.epilogue(np.array([[acc]], np.int32), np.array([s], np.float32),
+                         np.array([al], np.float32))[0, 0]
+        assert y.view(np.uint32) == y_ref.view(np.uint32), (acc, s, al)
+        assert (np.float32(acc) * al) * s != y_ref and np.float32(acc) * (s * al) != y_ref
+
+
+def test_parallel_oracle_build_gives_identical_products(orc):
+    rng = np.random.default_rng(12)
+    q = rng.integers(-128, 128, (5, 640)).astype(np.int8)
+    T = orc.quantize(rng.normal(0, 0.02, (300, 640)).astype(np.float32))[0]
+    assert np.array_equal(orc.gemm_i32(q, T), orc.gemm_i32(q, T, parallel=True))
+    assert orc.threads(parallel=False) == 1

@@ -96,6 +96,99 @@ def test_act_quant_ties_golden(orc):
     assert float(gs[0]) == 1.0
 
 
+def _golden_helpers():
+    import os
+    import sys
+    gdir = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    if gdir not in sys.path:
+        sys.path.insert(0, gdir)
+    import exact_fp32
+    return gdir, exact_fp32
+
+
+def test_act_quant_scaled_golden(orc):
+    """Scales other than 1 (golden from exact rational arithmetic): the GPU
+    quantizer, and sherry_linear's fused quantizer through its product, follow
+    one fp32 division x/s and round-half-even of that quotient."""
+    import os
+    gdir, ex = _golden_helpers()
+    rows, cur = [], {}
+    with open(os.path.join(gdir, "act_quant_scaled.txt")) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            key, val = line.split(":", 1)
+            cur[key.strip()] = val.split()
+            if key.strip() == "q":
+                rows.append(([ex.from_hex(v) for v in cur["x"]], ex.from_hex(cur["s"][0]),
+                             [int(v) for v in cur["q"]]))
+                cur = {}
+    x = torch.tensor(np.array([r[0] for r in rows], np.float32))
+    gq, gs = bw.quantize_act(x.cuda())
+    torch.cuda.synchronize()
+    for m, (_, s_ref, q_ref) in enumerate(rows):
+        assert gq[m].cpu().numpy().tolist() == q_ref, f"token {m}"
+        assert gs[m].cpu().numpy().view(np.uint32) == np.float32(s_ref).view(np.uint32)
+    # fused form (M = 3 <= 4 tokens): y must equal the oracle's product of the golden q
+    M, K = x.shape
+    N = 64
+    W = synth.weights(N, K, 0.02, False, seed=4242)
+    T, alpha = orc.quantize(W.numpy())
+    packed, galpha = gpu_pack(W)
+    assert bw.linear_plan(M, N, K)["fused"]
+    q_ref = np.array([r[2] for r in rows], np.int8)
+    s_ref = np.array([r[1] for r in rows], np.float32)
+    _, y_ref = orc.gemm(q_ref, s_ref, T, alpha)
+    gy = bw.linear(x.cuda(), packed, galpha, N, K).cpu().numpy()
+    assert np.array_equal(gy.view(np.uint32), y_ref.view(np.uint32))
+
+
+def test_epilogue_order_golden_every_path(orc):
+    """y[i,i] = ((float)acc * s_x[i]) * alpha[i] for crafted accumulators that
+    take the golden's values (exact rational arithmetic; each case one where
+    the other two multiplication orders round differently), on every path."""
+    import os
+    gdir, ex = _golden_helpers()
+    cases = []
+    with open(os.path.join(gdir, "epilogue_order.txt")) as f:
+        for line in f:
+            if line.startswith("case:"):
+                a, s_, al, y_ = line.split(":", 1)[1].split()
+                cases.append((int(a), ex.from_hex(s_), ex.from_hex(al), ex.from_hex(y_)))
+    C = len(cases)
+    # every weight row is the block (+1,+1,+1,0) repeated, so acc[m,n] is the
+    # sum of each block's first three q of token m, whatever n
+    K = 88 * 128                                # 2816 blocks x 381 >= max |acc|
+    W = torch.tensor([1.0, 1.0, 1.0, 0.0]).repeat(C, K // 4)
+    T, alpha = orc.quantize(W.numpy())
+    packed, _ = gpu_pack(W)
+    q = np.zeros((C, K), np.int8)
+    for m, (target, _, _, _) in enumerate(cases):
+        rem = target
+        for b in range(K // 4):
+            for j in range(3):
+                v = max(-127, min(127, rem))
+                q[m, 4 * b + j] = v
+                rem -= v
+        assert rem == 0
+    s_x = np.array([c[1] for c in cases], np.float32)
+    al = np.array([c[2] for c in cases], np.float32)
+    y_ref = np.array([c[3] for c in cases], np.float32)
+    acc, y_orc = orc.gemm(q, s_x, T, al)
+    assert np.array_equal(np.diag(acc), [c[0] for c in cases])
+    gq, gs, gal = torch.tensor(q).cuda(), torch.tensor(s_x).cuda(), torch.tensor(al).cuda()
+    for path, m0, m1 in [(None, 0, C), ("decode_mfma", 0, C), ("lut_gemv", 0, 16),
+                         ("decode_mfma_gemv", 16, 32), ("decode_mfma_gemv", 40, 41)]:
+        try:
+            bw.plan_override(path)
+            gy = bw.gemm(gq[m0:m1].contiguous(), gs[m0:m1].contiguous(), packed, gal, C, K).cpu().numpy()
+        finally:
+            bw.plan_override()
+        d = np.array([gy[i, m0 + i] for i in range(m1 - m0)], np.float32)
+        assert np.array_equal(d.view(np.uint32), y_ref[m0:m1].view(np.uint32)), path
+        assert np.array_equal(gy.view(np.uint32), y_orc[m0:m1].view(np.uint32)), path
+
+
 # ----------------------------------------------------- product, edge shapes
 SHAPES = [(64, 128), (192, 384), (320, 1152)]
 MS = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 64, 65, 100, 128, 129, 130]
@@ -332,18 +425,41 @@ def test_workload_parity(orc, name):
     _workload_check(orc, name)
 
 
-@pytest.mark.parametrize("bm", [0, 1])    # built-in tiles (128 tokens here), or 64 forced
-def test_workload_5_prefill_sampled(orc, bm):
+@pytest.fixture(scope="module")
+def workload_5_ref(orc):
+    """Workload 5 (M=512, K=4096, N=14336) and its full oracle product (the
+    same oracle source built with OpenMP over the host cores; identical sums)."""
     w = synth.WORKLOADS["5"]
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N - 1],
-                                     rng.choice(w.N, 251, replace=False)]))
+    W = synth.workload_weights(w)
+    x = synth.workload_activations(w)
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    _say(f"workload 5: full oracle product on {orc.threads(parallel=True)} threads")
+    acc, y = orc.gemm(q, s, T, alpha, parallel=True)
+    packed, galpha = gpu_pack(W)
+    assert np.array_equal(packed.cpu().numpy(), orc.pack(T)), "packed codes"
+    assert np.array_equal(galpha.cpu().numpy().view(np.uint32), alpha.view(np.uint32)), "alpha"
+    gq, gs = bw.quantize_act(x.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cpu().numpy(), q), "q"
+    assert np.array_equal(gs.cpu().numpy().view(np.uint32), s.view(np.uint32)), "s_x"
+    return w, acc, y, packed, galpha, gq, gs
+
+
+@pytest.mark.parametrize("bm", [0, 1, 2])    # built-in tiles, or 64 / 128 tokens forced
+def test_workload_5_prefill_full(workload_5_ref, bm):
+    """Every one of the 7.3 M outputs of workload 5: int32 bit-exact, fp32
+    within 1e-5 (bit-identical in practice)."""
+    w, acc, y, packed, galpha, gq, gs = workload_5_ref
     try:
         bw.plan_override("decode_mfma" if bm else None, bm)
-        _say(f"workload 5: {bw.plan(w.M, w.N, w.K)}")
-        _workload_check(orc, "5", sample_rows=rows)
+        _say(f"workload 5 full: {bw.plan(w.M, w.N, w.K)}")
+        gacc = bw.gemm_i32(gq, packed, w.N, w.K).cpu().numpy()
+        gy = bw.gemm(gq, gs, packed, galpha, w.N, w.K).cpu().numpy()
     finally:
         bw.plan_override()
+    assert np.array_equal(gacc, acc), "acc"
+    assert_y_close(gy, y)
 
 
 # ------------------------------------------------------ random shape sweep
