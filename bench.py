@@ -1,32 +1,37 @@
 """Benchmark of the Sherry 3:4 ternary matmul on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2a]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 
-A step is one pass of the hot path over one batch of synthetic input:
-per-token int8 quantization of the fp32 activations and the product with the
-packed weights, as one sherry_linear call (for the default workload the
-quantization runs inside the product kernel; sherry_quantize_act and
-sherry_gemm are also timed on their own).  Offline packing
-(sherry_quantize_pack) is timed separately and reported under "offline".
-Steps rotate over R copies of the packed weights whose total size exceeds
-twice the 256 MB last-level cache, so every step streams its weights from
-HBM; the K timed steps are captured once into a HIP graph and replayed, with
-HIP events (recorded on the stream the kernels run on) around the replay.
+A step is one pass of the hot path over one batch of synthetic input: the
+product of per-token int8 activations (quantized once, ahead of the timed
+region, as the product's input) with the packed 3:4 ternary weights and the
+float rescale, as one sherry_gemm call.  The default workload is the
+batched decode GEMV at a 70B-class MLP shape (M=8, K=8192, N=28672), the
+HBM-bound decode configuration.  Steps rotate over R copies of the packed
+weights whose total size exceeds twice the 256 MB last-level cache, so
+every step streams its weights from HBM; the K timed steps are captured
+once into a HIP graph and replayed, with HIP events (recorded on the stream
+the kernels run on) around the replay.
 
-Prints ONE JSON line.  `value` is packed-weight GB/s of the whole step
-(N*K*5/32 bytes per step / step time) on the default workload (decode GEMV,
-LLaMA-7B attention projection: M=1, K=4096, N=4096).  "roofline" is the
-dominant kernel against the 8 TB/s HBM peak: the step's one kernel when the
-quantization is fused into the product (as it is for this workload), else
-the product kernel the launch plan picks; "prefill" holds the M=512 decode + int8 MFMA
-product against the 5.0 POP/s int8 peak; "workloads" holds every workload's
-kernel time, and for M <= 16 the time of each small-M path (lookup-table
-GEMV and matrix-core GEMV); "mid_m" times M = 16..200 tokens at the prefill
-layer's shape on the planned path; "grouped_qkv" and "grouped_gate_up" time three
-(two) projections of one x as one call on stacked packed weights against
-separate calls; "two_bit_baseline" times the
-same ternary weights in the plain 2-bit packing.  "cpu_baseline" times the
-CPU oracle (single thread) on a bounded sample of the same workload.
+Prints ONE JSON line.  `value` is packed-weight GB/s (N*K*5/32 bytes per
+step / step time).  "roofline" is the step's one kernel against the 8 TB/s
+HBM peak: its algorithmic bytes (packed codes, alpha, int8 x and s_x, fp32
+y) over its per-launch time; "traffic" is HBM bytes per launch from the
+committed rocprofv3 counter summary when it still matches the kernel's
+sources and launch plan.  "ceilings" holds what this GPU reaches in the same
+process: a plain streaming read of the same rotating bytes, a large read, a
+device copy and an empty launch; every workload also carries the plain read
+of its own packed bytes ("read_floor_us").  "step_with_quantization" times
+sherry_linear (quantization + product) on the same workload.  "prefill"
+holds the M=512 decode + int8 MFMA product against the 5.0 POP/s int8 peak;
+"workloads" every workload's kernel time, and for M <= 16 the time of each
+small-M path (lookup-table GEMV and matrix-core GEMV); "mid_m" M = 16..200
+tokens at the prefill layer's shape; "grouped_qkv" and "grouped_gate_up"
+three (two) projections of one x as one call on stacked packed weights
+against separate calls; "two_bit_baseline" the same ternary weights in the
+plain 2-bit packing.  "cpu_baseline" times the CPU oracle on a bounded
+sample of the same workload: the same source built with OpenMP on all host
+cores, and single-threaded on one core.
 """
 
 from __future__ import annotations
@@ -45,6 +50,22 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
 MALL_BYTES = 256 << 20         # last-level (Infinity) cache
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "packed-weight GB/s (% HBM peak) for decode GEMV; int8 TOPS (% MFMA) prefill"
+WORKLOAD_NAMES = {
+    "1": "decode GEMV, M=1, K=256, N=256 (3:4 ternary W, per-token int8 x)",
+    "2a": "decode GEMV, LLaMA-7B attention projection: M=1, K=4096, N=4096",
+    "2b": "batched decode GEMV, LLaMA-7B attention projection: M=4, K=4096, N=4096",
+    "2c": "batched decode GEMV, LLaMA-7B attention projection: M=16, K=4096, N=4096",
+    "3a": "decode GEMV, LLaMA-7B MLP up/gate: M=1, K=4096, N=11008, spiky W",
+    "3b": "decode GEMV, LLaMA-7B MLP down: M=1, K=11008, N=4096, spiky W",
+    "4": "batched decode GEMV, 70B-class MLP shape: M=8, K=8192, N=28672 (3:4 ternary W, "
+         "per-token int8 x; HBM-bound)",
+    "5": "prefill GEMM: M=512, K=4096, N=14336 (decode -> int8 MFMA)",
+}
+
+
+def progress(msg: str) -> None:
+    """A progress line on stderr (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def parse():
@@ -52,7 +73,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="2a")
+    ap.add_argument("--workload", default="4")
     ap.add_argument("--copies", type=int, default=0, help="rotating weight copies (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -189,31 +210,134 @@ def traffic_from_profile(kernel: str, workload: str, plan: dict):
         return None
 
 
+def host_identity() -> dict:
+    """The CPU the oracle runs on: model name, logical CPUs, and the CPUs this
+    process may run on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(name: str, seconds: float):
-    """The CPU oracle (single-threaded C, as it stands) on the same workload:
-    per-token quantization + dense int8 x ternary product + epilogue, repeated
-    for a bounded number of whole steps."""
-    import numpy as np
+    """The CPU oracle as it stands on the same workload: per-token
+    quantization + dense int8 x unpacked-ternary product + epilogue, whole
+    steps repeated for about `seconds`, once with the same source built with
+    OpenMP (all host cores; the int32 sums are identical) and once
+    single-threaded on one core.  The headline is the all-core figure."""
     import oracle
     from bit_weight_amd import synth
     w = synth.WORKLOADS[name]
-    T, alpha = oracle.quantize(synth.workload_weights(w).numpy())
-    x = synth.workload_activations(w).numpy()
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        q, s = oracle.act_quant(x)
-        oracle.gemm(q, s, T, alpha)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 100000:
-            break
-    per = el / n
-    return {"value": round(w.packed_bytes / per / 1e9, 6), "unit": "GB/s", "cores": 1,
+    W = synth.workload_weights(w)
+    x = synth.workload_activations(w)
+    sha = {"W": synth.sha256(W), "x": synth.sha256(x)}
+    T, alpha = oracle.quantize(W.numpy())
+    del W
+    xn = x.numpy()
+
+    def run(parallel: bool):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            q, s = oracle.act_quant(xn)
+            oracle.gemm(q, s, T, alpha, parallel=parallel)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= 100000:
+                return n, el
+
+    threads = oracle.threads(parallel=True)
+    n_all, el_all = run(True)
+    n_one, el_one = run(False)
+    what = (f"workload {name} (M={w.M}, K={w.K}, N={w.N}): whole steps of act quant + dense int8 x "
+            f"unpacked-ternary product + epilogue")
+    per_all, per_one = el_all / n_all, el_one / n_one
+    return {"value": round(w.packed_bytes / per_all / 1e9, 6), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"workload {name} (M={w.M}, K={w.K}, N={w.N}): {n} whole steps "
-                      f"(act quant + dense int8 x unpacked-ternary product + epilogue) in "
-                      f"{el:.1f} s, {per * 1e3:.2f} ms/step; host {platform.processor() or platform.machine()}"}
+            "sample": f"{what}: {n_all} steps in {el_all:.1f} s ({per_all * 1e3:.1f} ms/step) on "
+                      f"{threads} OpenMP threads (the same oracle source built with -fopenmp)",
+            "single_core": {"value": round(w.packed_bytes / per_one / 1e9, 6), "unit": "GB/s",
+                            "cores": 1,
+                            "sample": f"{what}: {n_one} steps in {el_one:.1f} s "
+                                      f"({per_one * 1e3:.1f} ms/step), single-threaded build"},
+            "host": host_identity(), "inputs_sha256": sha,
+            "build": "g++ " + " ".join(oracle.CXXFLAGS) + " (all cores: + -fopenmp)"}
+
+
+READ_SHAPES = [(g, b, 4) for g in (256, 512, 1024, 2048) for b in (256, 512)]
+
+
+def read_floor(torch, bw, bufs, n: int):
+    """A plain streaming read of the same rotating buffers (one launch per
+    buffer in turn, replayed in a HIP graph): the best time per launch over a
+    few grid / block shapes, in us, and its shape."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = None
+    for grid, block, unroll in READ_SHAPES:
+        ms, _ = graph_time(torch, lambda i: bw.probe_read(bufs[i % len(bufs)], sink, grid, block, unroll),
+                           n, reps=2)
+        if best is None or ms < best[0]:
+            best = (ms, grid, block, unroll)
+    return round(best[0] * 1e3, 3), {"grid": best[1], "block": best[2], "unroll": best[3]}
+
+
+def ceilings(torch, bw, st):
+    """What this GPU reaches in the same process, beside which every number
+    is reported: the plain read of the step's own rotating weight copies, a
+    1 GiB read, a 512 MiB device copy and the empty-launch floor."""
+    out = {}
+    nb = st.w.packed_bytes
+    us, shape = read_floor(torch, bw, st.packed, max(200, st.R))
+    out["read_same_bytes"] = {"bytes_per_launch": nb, "us": us, "GB_s": round(nb / us / 1e3, 1),
+                              "rotating_copies": st.R, "shape": shape}
+    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = None
+    for grid in (1024, 2048, 4096, 8192):
+        for unroll in (4, 8):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for _ in range(3):
+                torch.cuda.synchronize()
+                e0.record()
+                bw.probe_read(big, sink, grid, 512, unroll)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1)
+                if best is None or ms < best[0]:
+                    best = (ms, grid, unroll)
+    out["read_1GiB"] = {"GB_s": round(big.numel() / best[0] / 1e6, 1), "ms": round(best[0], 4),
+                        "shape": {"grid": best[1], "block": 512, "unroll": best[2]}}
+    del big
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    out["copy_512MiB"] = {"GB_s_read_plus_write": round(2 * src.numel() / best / 1e6, 1),
+                          "ms": round(best, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
+    ms, _ = graph_time(torch, lambda i: bw.probe_empty(), 1000, reps=3)
+    out["empty_launch_us"] = round(ms * 1e3, 3)
+    return out
 
 
 def two_bit_bench(torch, bw, synth, five_bit_us: dict):
@@ -338,22 +462,23 @@ def main():
         return
 
     name = args.workload
+    progress(f"workload {name}: packing and rotating copies")
     st = Setup(torch, bw, synth, name, args.copies)
     w = st.w
     # correctness of graph replay against eager (replayed several times)
-    ref = st.step(bw, 0).clone()
+    ref = st.gemm(bw, 0).clone()
     torch.cuda.synchronize()
     # warmup steps, then the timed steps
     gw = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gw):
         for i in range(args.warmup):
-            st.step(bw, i)
+            st.gemm(bw, i)
     gw.replay()
     torch.cuda.synchronize()
     gt = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gt):
         for i in range(args.steps):
-            st.step(bw, i)
+            st.gemm(bw, i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -361,35 +486,27 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / args.steps
+    # every step wrote y from the same x: the last replayed copy's output
+    # equals the eager first call's (all copies hold the same weights)
     ok = bool(torch.equal(st.y, ref))
-    st.step(bw, 1)                  # eager work between replays
+    st.gemm(bw, 1)                  # eager work between replays
     torch.cuda.synchronize()
     gt.replay()
     torch.cuda.synchronize()
     ok = ok and bool(torch.equal(st.y, ref))
 
-    # dominant kernel alone: back-to-back products over the rotating copies
-    n_k = max(args.steps, st.R)
-    gemm_ms, _ = graph_time(torch, lambda i: st.gemm(bw, i), n_k, reps=3)
-    act_ms, _ = graph_time(torch, lambda i: bw.quantize_act(st.x), n_k, reps=3)
     plan = bw.plan(w.M, w.N, w.K)
-    lplan = bw.linear_plan(w.M, w.N, w.K)
-    fused = lplan["fused"]
-    if fused:
-        # the step is one kernel (quantization fused into the product, on
-        # sherry_linear's own plan): its duration is the timed region's
-        # per-step time, and its algorithmic bytes read the fp32 activations
-        kern = PATH_KERNEL[lplan["path"]]
-        alg = algorithmic_bytes(w, fp32_x=True)
-        kern_ms = step_ms
-        traffic = traffic_from_profile(kern + "_fused", name, lplan)
-    else:
-        kern = PATH_KERNEL[plan["path"]]
-        alg = algorithmic_bytes(w)
-        kern_ms = gemm_ms
-        traffic = traffic_from_profile(kern, name, plan)
-    achieved = alg / kern_ms / 1e6
+    kern = PATH_KERNEL[plan["path"]]
+    alg = algorithmic_bytes(w)
+    traffic = traffic_from_profile(kern, name, plan)
+    # the step is one launch of the product kernel: its duration is the timed
+    # region's per-step time
+    achieved = alg / step_ms / 1e6
     value = w.packed_bytes / step_ms / 1e6
+    n_k = max(args.steps, st.R)
+    lin_ms, _ = graph_time(torch, lambda i: st.step(bw, i), n_k, reps=3)
+    act_ms, _ = graph_time(torch, lambda i: bw.quantize_act(st.x), n_k, reps=3)
+    lplan = bw.linear_plan(w.M, w.N, w.K)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -403,38 +520,43 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "decode GEMV, LLaMA-7B attention projection (3:4 ternary W, "
-                               "per-token int8 x)",
+        "config": {"workload": WORKLOAD_NAMES.get(name, f"workload {name}"),
                    "M": w.M, "K": w.K, "N": w.N, "weights": f"Normal(0,{w.w_std})",
+                   "activations": "Normal(0,1), per-token int8 (quantized before the timed region)",
                    "rotating_copies": st.R,
-                   "step": "sherry_linear (per-token int8 quantization + product)",
-                   "linear_fused": fused,
-                   "plan": {k: v for k, v in lplan.items() if k != "fused"},
-                   "gemm_plan": plan, "parallelism": "none (1 GPU)"},
+                   "step": "sherry_gemm (int8 x, s_x, packed weights, alpha -> fp32 y)",
+                   "plan": plan, "parallelism": "none (1 GPU)"},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": f"{kern}_kernel" + (" (fused quantization)" if fused else ""),
-                     "kernel_us": round(kern_ms * 1e3, 3), "bytes_per_launch": alg,
+                     "traffic": traffic, "kernel": f"{kern}_kernel",
+                     "kernel_us": round(step_ms * 1e3, 3), "bytes_per_launch": alg,
                      "packed_bytes_per_launch": w.packed_bytes},
-        "kernels_us": {"sherry_gemm": round(gemm_ms * 1e3, 3),
-                       "sherry_quantize_act": round(act_ms * 1e3, 3)},
+        "step_with_quantization": {"call": "sherry_linear (fp32 x: per-token quantization + product)",
+                                   "us": round(lin_ms * 1e3, 3), "fused": lplan["fused"],
+                                   "sherry_quantize_act_us": round(act_ms * 1e3, 3)},
         "graph_replay_matches_eager": ok,
         "offline": {"sherry_quantize_pack_ms": round(st.pack_ms, 3),
                     "pack_input_GB_s": round(4 * w.N * w.K / st.pack_ms / 1e6, 1)},
     }
+    progress(f"step {step_ms * 1e3:.3f} us; ceilings")
+    out["ceilings"] = ceilings(torch, bw, st)
+    rs = out["ceilings"]["read_same_bytes"]["us"]
+    out["roofline"]["vs_read_same_bytes"] = round(rs / (step_ms * 1e3), 4)
     del st
     torch.cuda.empty_cache()
 
     if not args.no_extra:
         wl = {}
         for nm in ("1", "2a", "2b", "2c", "3a", "3b", "4", "5"):
+            progress(f"workload {nm}")
             s2 = Setup(torch, bw, synth, nm, 0)
             ms, _ = graph_time(torch, lambda i: s2.gemm(bw, i), max(200, s2.R), reps=3)
             ww = s2.w
+            rf_us, rf_shape = read_floor(torch, bw, s2.packed, max(200, s2.R))
             ent = {"M": ww.M, "K": ww.K, "N": ww.N, "kernel_us": round(ms * 1e3, 3),
-                   "plan": bw.plan(ww.M, ww.N, ww.K), "rotating_copies": s2.R}
+                   "plan": bw.plan(ww.M, ww.N, ww.K), "rotating_copies": s2.R,
+                   "read_floor_us": rf_us, "read_floor_shape": rf_shape}
             if ww.M <= 16:
                 # every small-M path on the same launches (the default is one of them)
                 alt = {}
@@ -462,11 +584,12 @@ def main():
         out["prefill"] = {"workload": "prefill GEMM M=512 K=4096 N=14336",
                           "value": p5["TOPS"], "unit": "TOPS",
                           "roofline": {"bound": "mfma", "achieved": p5["TOPS"],
-                                       "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                                       "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                                        "frac": p5["mfma_frac"],
                                        "traffic": traffic_from_profile(
                                            "mfma_gemm", "5", p5["plan"]),
                                        "kernel": "mfma_gemm_kernel"}}
+        progress("mid M, grouped projections, 2-bit baseline")
         out["mid_m"] = mid_m_bench(torch, bw, synth)
         torch.cuda.empty_cache()
         out["grouped_qkv"] = grouped_bench(torch, bw, synth, "2a", 3)
@@ -476,6 +599,7 @@ def main():
             torch, bw, synth, {k: v["path_us"]["decode_mfma_gemv"] for k, v in wl.items() if "path_us" in v})
         torch.cuda.empty_cache()
     if not args.no_cpu:
+        progress("CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

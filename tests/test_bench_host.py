@@ -80,3 +80,26 @@ def test_more_than_one_gpu_is_refused(n):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", n],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_default_workload_is_the_hbm_bound_decode_shape():
+    """The headline is the batched decode GEMV at the 70B-class MLP shape
+    (M=8, K=8192, N=28672), the HBM-bound decode configuration."""
+    assert bench.parse.__code__ is not None
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        args = bench.parse()
+    finally:
+        sys.argv = old
+    assert args.workload == "4"
+    w = synth.WORKLOADS[args.workload]
+    assert (w.M, w.K, w.N) == (8, 8192, 28672)
+    assert w.packed_bytes == 36_700_160
+    assert bench.algorithmic_bytes(w) == 36_700_160 + 4 * 28672 + (8 * 8192 + 4 * 8) + 4 * 8 * 28672
+    assert set(bench.WORKLOAD_NAMES) == set(synth.WORKLOADS)
+
+
+def test_host_identity_names_the_cpu():
+    h = bench.host_identity()
+    assert h["cpu_model"] and h["nproc"] >= 1 and 1 <= h["usable_cpus"] <= h["nproc"]
