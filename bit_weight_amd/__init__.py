@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
                 "sherry_gemm2_workspace_bytes": ([i64, i64, i64], sz),
                 "sherry_gemm2": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], ci),
                 "sherry_linear": ([vp, vp, vp, vp, i64, i64, i64, vp, sz, vp, sz, vp], ci),
+                "sherry_gemm_noalloc": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], ci),
                 "sherry_probe_read": ([vp, sz, vp, ci, ci, ci, vp], ci),
                 "sherry_probe_empty": ([vp], ci),
             }
@@ -251,6 +252,31 @@ def gemm_i32(x: torch.Tensor, packed: torch.Tensor, N: int, K: int,
     wn = ws.numel() if ws is not None else 0
     _check(lib().sherry_gemm_i32(px, packed.data_ptr(), pa, M, N, K, wp, wn, _stream(x.device)),
            "sherry_gemm_i32")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # the static split-K scratch of sherry_gemm_noalloc, per GPU
+
+
+def gemm_noalloc(x: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor,
+                 N: int, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """sherry_gemm without a workspace (sherry_gemm_noalloc): the split-K
+    cells live in the library's static per-GPU array; shapes needing more
+    than 8 MiB of them are rejected.  Calls that overlap on one GPU race."""
+    px = _dev_tensor(x, "x", torch.int8)
+    _dev_tensor(packed, "packed", torch.uint8)
+    _dev_tensor(s_x, "s_x", torch.float32)
+    _dev_tensor(alpha, "alpha", torch.float32)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise RuntimeError(f"x must be [M,{K}]")
+    if packed.numel() != packed_bytes(N, K):
+        raise RuntimeError("packed has the wrong size for [N,K]")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    py = _dev_tensor(out, "out", torch.float32)
+    _check(lib().sherry_gemm_noalloc(px, s_x.data_ptr(), packed.data_ptr(), alpha.data_ptr(), py, M, N, K,
+                                     _stream(x.device)), "sherry_gemm_noalloc")
     return out
 
 

@@ -260,7 +260,65 @@ sherry_status run_gemm(const int8_t* x, const float* s_x, const void* packed, co
 
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
+}  // namespace
 
+// ---------------------------------------------------------------------------
+// Static split-K scratch of sherry_gemm_noalloc, for callers that cannot
+// allocate device memory.  Each GPU the library runs on holds its own copy
+// of this array until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device array: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever passed to a kernel.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned long long scratch[kNoAllocScratchBytes / sizeof(unsigned long long)];
+
+namespace {
+
+// Zero-fills n16 16-byte chunks (a kernel, not hipMemsetAsync, so that a
+// call under graph capture records a kernel node).
+__global__ void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct NoAllocScratch {
+  std::mutex mu;
+  bool resolved = false;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;     // device address of this device's `scratch`
+  bool cleared = false;    // a clear has run eagerly (outside graph capture)
+};
+NoAllocScratch g_noalloc[kMaxDevices];
+
+// The current device's scratch address.  The first call on a device resolves
+// it, and until one call has run outside graph capture every call first
+// enqueues a zero fill of the whole array on its own stream (the product's
+// split-K cells must start at zero; every completed product leaves its
+// cells zero again, so later calls need no clear).
+sherry_status noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SHERRY_ERR_HIP;
+  if (dev >= kMaxDevices) return SHERRY_ERR_DEVICE;
+  NoAllocScratch& st = g_noalloc[dev];
+  std::lock_guard<std::mutex> lock(st.mu);
+  if (!st.resolved) {
+    void* p = nullptr;
+    st.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    st.ptr = st.err == hipSuccess ? p : nullptr;
+    st.resolved = true;
+  }
+  if (st.err != hipSuccess || !st.ptr) return SHERRY_ERR_HIP;
+  if (!st.cleared) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SHERRY_ERR_HIP;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(512), dim3(256), 0, stream, static_cast<uint4*>(st.ptr),
+                       kNoAllocScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return SHERRY_ERR_HIP;
+    if (cap == hipStreamCaptureStatusNone) st.cleared = true;
+  }
+  *out = st.ptr;
+  return SHERRY_OK;
+}
 
 // Scratch of sherry_linear: q [M,K] and s_x [M] when the quantization is
 // not fused into the product (any content; not kept zero).
@@ -385,6 +443,39 @@ sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           size_t workspace_bytes, void* stream) {
   if (!y) return SHERRY_ERR_NULL;
   return run_gemm(x, s_x, packed, alpha, y, nullptr, M, N, K, workspace, workspace_bytes, stream);
+}
+
+sherry_status sherry_gemm_noalloc(const int8_t* x, const float* s_x, const void* packed,
+                                  const float* alpha, float* y, int64_t M, int64_t N, int64_t K,
+                                  void* stream) {
+  if (!x || !s_x || !packed || !alpha || !y) return SHERRY_ERR_NULL;
+  if (!shape_ok(M, N, K)) return SHERRY_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || !aligned(s_x, 4) ||
+      !aligned(alpha, 4))
+    return SHERRY_ERR_ALIGN;
+  const GemmPlan plan = plan_gemm((int)M, (int)N, (int)K);
+  if (plan.ws_bytes > kNoAllocScratchBytes) return SHERRY_ERR_WORKSPACE;
+  const sherry_status d = check_device();
+  if (d != SHERRY_OK) return d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GemmArgs args{};
+  args.x = x;
+  args.s_x = s_x;
+  args.packed = static_cast<const uint8_t*>(packed);
+  args.alpha = alpha;
+  args.y = y;
+  args.M = (int)M;
+  args.N = (int)N;
+  args.K = (int)K;
+  if (plan.ws_bytes > 0) {
+    void* cells = nullptr;
+    const sherry_status st = noalloc_scratch(s, &cells);
+    if (st != SHERRY_OK) return st;
+    args.partials = static_cast<int32_t*>(cells);
+  }
+  bool partial = false;
+  const hipError_t e = launch_product(plan, args, s, &partial);
+  return e == hipSuccess ? SHERRY_OK : (partial ? SHERRY_ERR_PARTIAL : SHERRY_ERR_HIP);
 }
 
 sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc, int64_t M, int64_t N,

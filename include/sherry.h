@@ -142,6 +142,26 @@ sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           int64_t K, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* The same product as sherry_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no workspace argument.  When the plan splits K, the
+ * split-K cells live in a static device array of the library, 8 MiB per
+ * GPU (held until the process ends), so shapes whose
+ * sherry_workspace_bytes(M,N,K) exceeds 8 MiB (8388608) are rejected with
+ * SHERRY_ERR_WORKSPACE before anything is enqueued.  The call allocates
+ * nothing and calls no allocating routine.
+ *   Arguments, alignment, shapes and results: as sherry_gemm (identical y).
+ *   The first call on a device resolves the array's device address; until
+ *   one call has run outside graph capture, each call first enqueues a
+ *   zero fill of the array (one extra small kernel) on its stream.  Every
+ *   completed call leaves the array zero again.
+ *   Every call on one GPU shares that GPU's array: calls that can overlap
+ *   on one GPU (different streams, or different threads without ordering)
+ *   race and may return wrong sums; serialize them on one stream. */
+sherry_status sherry_gemm_noalloc(const int8_t* x, const float* s_x, const void* packed,
+                                  const float* alpha, float* y, int64_t M, int64_t N,
+                                  int64_t K, void* stream);
+
 /* Same product, stopping at the int32 accumulators: acc [M,N] int32
  * (written, 16-byte aligned).  Same kernels and workspace rules. */
 sherry_status sherry_gemm_i32(const int8_t* x, const void* packed, int32_t* acc,

@@ -346,3 +346,35 @@ def test_plan_invariants_over_random_shapes():
             assert M <= 4 and M * K <= 16384, (M, N, K, lp)
             assert -(-KT // lp["splits"]) <= 32 and lp["block"] <= 1024
             assert bw.workspace_bytes(M, N, K) >= (M * N * 8 if lp["splits"] > 1 else 0)
+
+
+# ------------------------------------------------ sherry_gemm_noalloc (host)
+def _noalloc(**kw):
+    a = dict(x=FAKE, s=FAKE, p=FAKE, al=FAKE, y=FAKE, M=1, N=64, K=128)
+    a.update(kw)
+    return bw.lib().sherry_gemm_noalloc(a["x"], a["s"], a["p"], a["al"], a["y"], a["M"], a["N"], a["K"],
+                                        None)
+
+
+def test_noalloc_argument_errors():
+    for k in ("x", "s", "p", "al", "y"):
+        assert _noalloc(**{k: None}) == NULL, k
+    assert _noalloc(M=0) == SHAPE and _noalloc(K=100) == SHAPE and _noalloc(N=65) == SHAPE
+    assert _noalloc(x=FAKE + 4) == ALIGN and _noalloc(y=FAKE + 4) == ALIGN and _noalloc(p=FAKE + 8) == ALIGN
+
+
+def test_noalloc_rejects_shapes_beyond_its_static_scratch():
+    """The static split-K scratch holds 8 MiB per GPU: a plan whose cells
+    need more is refused on the host, before anything is enqueued."""
+    assert bw.NOALLOC_SCRATCH_BYTES == 8 << 20
+    try:
+        # force a K-split on a wide shape: 32 x 65536 cells of 8 bytes = 16 MiB
+        bw.plan_override("decode_mfma_gemv", 4, 0, 2)
+        assert bw.workspace_bytes(32, 65536, 256) == 16 << 20
+        assert _noalloc(M=32, N=65536, K=256) == WS
+        # 16 x 65536 cells are exactly 8 MiB: accepted by the size check (the
+        # call then needs the device, which this host has not)
+        assert bw.workspace_bytes(16, 65536, 256) == 8 << 20
+        assert _noalloc(M=16, N=65536, K=256) not in (WS, SHAPE, ALIGN, NULL)
+    finally:
+        bw.plan_override()
