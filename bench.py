@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="only the default workload")
     ap.add_argument("--only", default="", help="profile mode: run only these workloads' "
                     "product launches (comma list), print timings, no JSON contract line")
+    ap.add_argument("--path", default="", choices=("", "lut_gemv", "decode_mfma_gemv", "decode_mfma"),
+                    help="profile mode: force this path for the --only launches (default: the built-in plan)")
     return ap.parse_args()
 
 
@@ -449,6 +451,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        if args.path:
+            bw.plan_override(args.path)
         for name in args.only.split(","):
             st = Setup(torch, bw, synth, name, args.copies)
             n = max(args.steps, st.R)

@@ -190,11 +190,20 @@ GemmPlan plan_gemm(int M, int N, int K) {
   int ch_max = 1;                       // one stage of tables stays <= 32 KB
   while (ch_max < 8 && (ch_max * 2) * MP <= 8) ch_max *= 2;
 
-  int rw = g_ovr_rw.load() > 0 ? g_ovr_rw.load() : 4;
+  // Built-in plan from a sweep of row tiles per workgroup x table stage x
+  // K-splits on MI355X (M=1 at K=4096 and 11008, M=4 and 16 at K=N=4096,
+  // M=8 at K=8192, N=28672): up to 4 tokens, one row tile per workgroup
+  // (its 4 waves share it); above, 4 row tiles of one wave each.  K-splits
+  // of 2 k-tiles for 1-2 tokens and above 8, else 4, at most 16 splits:
+  // more workgroups keep more lookups in flight, and the 64-bit cell
+  // atomics of the splits cost less than idle CUs (M=16: 24.3 -> 17.4 us,
+  // M=4: 8.0 -> 6.1, M=8 at N=28672: 42.7 -> 33.8 against 512 workgroups).
+  int rw = g_ovr_rw.load() > 0 ? g_ovr_rw.load() : (M > 4 ? 4 : 1);
   if (rw != 1 && rw != 2 && rw != 4) rw = 4;
   const int G = (RT + rw - 1) / rw;
-  constexpr int kTargetWorkgroups = 512;
-  int splits = g_ovr_splits.load() > 0 ? g_ovr_splits.load() : (kTargetWorkgroups + G - 1) / G;
+  const int kt_per_split_def = (M <= 2 || M > 8) ? 2 : 4;
+  int splits = g_ovr_splits.load() > 0 ? g_ovr_splits.load() : KT / kt_per_split_def;
+  if (splits > 16 && g_ovr_splits.load() <= 0) splits = 16;
   if (splits > KT) splits = KT;
   if (splits < 1) splits = 1;
   const int kt_per_split = (KT + splits - 1) / splits;
