@@ -26,7 +26,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsherry.so")
+# SHERRY_LIB names another build of the same library (the host-only
+# sanitizer build that the CPU tests make); by default the in-tree one
+LIB_PATH = os.environ.get("SHERRY_LIB") or os.path.join(_HERE, "libsherry.so")
 
 STATUS = {
     0: "SHERRY_OK", -1: "SHERRY_ERR_NULL", -2: "SHERRY_ERR_SHAPE",

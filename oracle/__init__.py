@@ -21,10 +21,13 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sherry_oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# SHERRY_ORACLE_LIBDIR names a folder holding other builds of both
+# libraries (the sanitizer builds of the CPU tests); by default this one
+_LIBDIR = os.environ.get("SHERRY_ORACLE_LIBDIR") or _HERE
+_LIB = os.path.join(_LIBDIR, "liboracle.so")
 # the same source built with OpenMP: only the int32 product runs on several
 # threads (its outputs are independent sums, so the values are identical)
-_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
+_LIB_OMP = os.path.join(_LIBDIR, "liboracle_omp.so")
 CXXFLAGS = ["-std=c++17", "-O2", "-fno-fast-math", "-ffp-contract=off",
             "-shared", "-fPIC"]
 OMP_FLAGS = ["-fopenmp"]

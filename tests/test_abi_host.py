@@ -57,6 +57,26 @@ def test_packed_bytes():
     assert bw.lib().sherry_packed2_bytes(68, 144) == 2 * 2 * 2048
 
 
+def test_sizes_at_the_int64_extremes_are_rejected():
+    """Size queries and plans return 0 / SHERRY_ERR_SHAPE for sizes near the
+    int64 limits and for negative ones, without overflowing on the way (the
+    sanitizer build of this library runs this test too)."""
+    L = bw.lib()
+    extremes = [2 ** 31 - 1, 2 ** 31, 2 ** 32 + 128, 2 ** 40, 2 ** 62, 2 ** 63 - 1, -1, -(2 ** 63)]
+    out = [ctypes.c_int() for _ in range(6)]
+    refs = [ctypes.byref(v) for v in out]
+    for a in extremes:
+        for b in (64, 128, a):
+            assert L.sherry_packed_bytes(a, b) == 0 and L.sherry_packed_bytes(b, a) == 0, (a, b)
+            assert L.sherry_packed2_bytes(a, b) == 0 and L.sherry_packed2_bytes(b, a) == 0, (a, b)
+            assert L.sherry_workspace_bytes(8, a, b) == 0 and L.sherry_workspace_bytes(a, 64, 128) == 0
+            assert L.sherry_linear_scratch_bytes(a, b, 128) == 0, (a, b)
+            assert L.sherry_gemm_plan(a, 64, 128, *refs[:5]) == SHAPE, (a, b)
+            assert L.sherry_gemm_plan(8, a, b, *refs[:5]) == SHAPE, (a, b)
+            assert L.sherry_linear_plan(a, b, 128, *refs) == SHAPE, (a, b)
+            assert _gemm(M=a, N=b, K=128) == SHAPE and _gemm(M=1, N=64, K=a) == SHAPE, (a, b)
+
+
 def test_plan_dispatch_rule():
     for M in (1, 2, 3, 8, 15, 16):
         assert bw.plan(M, 4096, 4096)["path"] in ("lut_gemv", "decode_mfma_gemv")
