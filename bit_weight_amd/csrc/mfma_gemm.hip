@@ -190,8 +190,11 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   // (32-bit words: every view below is a character type or 32-bit lanes)
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsBytes / 4];
   // the pair table in an array of its own: the compiler then sees that its
-  // lookups cannot read what an activation copy in flight is writing
-  __shared__ __attribute__((aligned(16))) uint2 dec2[1024];
+  // lookups cannot read what an activation copy in flight is writing.  Its
+  // alignment places it first in LDS, below 64 KB, so a lookup's table base
+  // folds into the instruction's offset field instead of costing a VALU OR
+  // per lookup (measured at M=512, K=4096, N=14336: 32.7 -> 31.9 us)
+  __shared__ __attribute__((aligned(1024))) uint2 dec2[1024];
   __shared__ float sxs[kBM];   // s_x of this tile's rows (epilogue)
 
   const int KT = k_tiles(K), RT = row_tiles(N);

@@ -37,10 +37,16 @@
 //    bit-identical to it), quantizes the k-tiles of its K-split into LDS and
 //    reads the A operands from there; this saves the quantizer's launch and
 //    its round trip through memory on the decode path.
-//  * Codes and activations are prefetched four k-tiles ahead into four
-//    register stages used in turn (three or two with several token blocks),
-//    so each wave keeps ~5 KB of its codes in flight (HBM streaming needs
-//    bytes in flight x latency to cover the bandwidth).
+//  * Codes and activations are prefetched into register stages used in
+//    turn: four (three or two with several token blocks) in the looped
+//    form, so each wave keeps ~5 KB of its codes in flight (HBM streaming
+//    needs bytes in flight x latency to cover the bandwidth); two in the
+//    straight-line form, whose grids are large enough that the loads of
+//    all waves saturate HBM anyway: there every wave must issue its first
+//    stages before it decodes anything, and at launch the memory system
+//    accepts them only as fast as it serves them (per-wave clock stamps at
+//    M=8, K=8192, N=28672: ~2.3 us median from entry to the first decode
+//    with four stages).
 #include "sherry_device.h"
 #include "sherry_launch.h"
 
@@ -51,6 +57,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kBlk = kTileRows / 16;   // MFMA column blocks per wave
+constexpr int kSL = 8;                 // most k-tiles per wave of the straight-line form
 constexpr int kRedLd = kTileRows + 4;  // words per token row of the epilogue tile
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, size_t bytes) {
@@ -368,17 +375,17 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
     __builtin_amdgcn_sched_barrier(0);
   };
   if constexpr (SL) {
-    // at most 2 * kStages k-tiles per wave: straight-line steps, so no loop
-    // carries the in-flight stage registers around a back edge (there the
-    // compiler copies them into place, waiting for every load).  Past the
-    // wave's last k-tile only the arithmetic is skipped; the refills are
-    // issued regardless (re-reading its last tile), so no branch merges the
-    // stage registers.
+    // at most kSL k-tiles per wave: straight-line steps, so no loop carries
+    // the in-flight stage registers around a back edge (there the compiler
+    // copies them into place, waiting for every load).  Past the wave's
+    // last k-tile only the arithmetic is skipped; the refills are issued
+    // regardless (re-reading its last tile), so no branch merges the stage
+    // registers.
 #pragma unroll
-    for (int i = 0; i < 2 * kStages; ++i) {
+    for (int i = 0; i < kSL; ++i) {
       const int st = i % kStages;
       if (i < nk) step(i, false, cw[st], ch[st], xa[st], xb[st]);
-      if (i + kStages < 2 * kStages) load(i + kStages, cw[st], ch[st], xa[st], xb[st]);
+      if (i + kStages < kSL) load(i + kStages, cw[st], ch[st], xa[st], xb[st]);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -487,23 +494,26 @@ hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     // straight-line steps for one token block with no K-split and 4 to 8
     // k-tiles per wave (measured at M=8, K=8192, N=28672: 13.4 -> 12.2 us;
     // with fewer k-tiles the loop never takes its back edge, and with
-    // several token blocks it was 2 % slower)
+    // several token blocks it was 2 % slower), with two register stages
+    // (against four, measured on MI355X: M=8, K=8192, N=28672 12.5 ->
+    // 11.9 us; M=16, K=4096, N=14336 6.8 -> 6.1; M=1, K=4096, N=11008
+    // 4.99 -> 4.73; no shape slower)
     const int nkw = (p.kt_per_split + KW - 1) / KW;
-    const bool sl4 = p.splits == 1 && nkw >= 4 && nkw <= 8;
+    const bool sl4 = p.splits == 1 && nkw >= 4 && nkw <= kSL;
 #define SHERRY_GEMV(MT_, MB_, ST_, SX_, SL_) \
   launch_product_kernel(mfma_gemv_kernel<KW, MT_, MB_, false, FMT, ST_, 1, SX_, SL_>, grid, block, 0, stream, a, p.splits, p.kt_per_split)
     if (a.M <= 1 && p.kt_per_split <= kFuseMaxSpan) {
-      if (sl4) SHERRY_GEMV(1, 1, 4, true, true); else SHERRY_GEMV(1, 1, 4, true, false);
+      if (sl4) SHERRY_GEMV(1, 1, 2, true, true); else SHERRY_GEMV(1, 1, 4, true, false);
     } else if (a.M <= 1) {
-      if (sl4) SHERRY_GEMV(1, 1, 4, false, true); else SHERRY_GEMV(1, 1, 4, false, false);
+      if (sl4) SHERRY_GEMV(1, 1, 2, false, true); else SHERRY_GEMV(1, 1, 4, false, false);
     } else if (a.M <= 2) {
-      if (sl4) SHERRY_GEMV(2, 1, 4, false, true); else SHERRY_GEMV(2, 1, 4, false, false);
+      if (sl4) SHERRY_GEMV(2, 1, 2, false, true); else SHERRY_GEMV(2, 1, 4, false, false);
     } else if (a.M <= 4) {
-      if (sl4) SHERRY_GEMV(4, 1, 4, false, true); else SHERRY_GEMV(4, 1, 4, false, false);
+      if (sl4) SHERRY_GEMV(4, 1, 2, false, true); else SHERRY_GEMV(4, 1, 4, false, false);
     } else if (a.M <= 8) {
-      if (sl4) SHERRY_GEMV(8, 1, 4, false, true); else SHERRY_GEMV(8, 1, 4, false, false);
+      if (sl4) SHERRY_GEMV(8, 1, 2, false, true); else SHERRY_GEMV(8, 1, 4, false, false);
     } else if (a.M <= 16) {
-      if (sl4) SHERRY_GEMV(16, 1, 4, false, true); else SHERRY_GEMV(16, 1, 4, false, false);
+      if (sl4) SHERRY_GEMV(16, 1, 2, false, true); else SHERRY_GEMV(16, 1, 4, false, false);
     } else if constexpr (FMT == 0 && KW <= 8) {   // 16 waves leave too few registers for two blocks
       if (a.M <= 32) {
         SHERRY_GEMV(16, 2, 3, false, false);
