@@ -196,6 +196,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   // per lookup (measured at M=512, K=4096, N=14336: 32.7 -> 31.9 us)
   __shared__ __attribute__((aligned(1024))) uint2 dec2[1024];
   __shared__ float sxs[kBM];   // s_x of this tile's rows (epilogue)
+  // arrivals at the step barrier of each k-tile parity (128-row tiles)
+  __shared__ unsigned parity_arrivals[2];
 
   const int KT = k_tiles(K), RT = row_tiles(N);
   // tile id -> (m tile, n tile): consecutive ids of one XCD share n tiles
@@ -213,6 +215,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   const int wave = wv & 3, kh = wv >> 2;            // row tile, k-tile parity
   const int l16 = lane & 15, g = lane >> 4;
 
+  if (tid < 2) parity_arrivals[tid] = 0u;   // published by the prologue's barrier
   // decode table: code pair (c0 | c1 << 5) -> the 8 int8 weights of both
   for (int i = tid; i < 1024; i += kThreads)
     dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
@@ -299,13 +302,37 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   // decoded during step j-1; the register stage (wn, hn) holds the codes of
   // step j+1, decoded during this step's MFMAs into bn0 / bn1 and then
   // refilled with the codes of step j+3.
+  // The step barrier.  With 128-row tiles it joins only the 4 waves of this
+  // wave's k-tile parity, which share that parity's activation buffers and
+  // nothing else until the epilogue: an LDS arrival count per parity, so the
+  // two parities' waves (two to a SIMD) need not leave each step together
+  // (measured at N=14336, K=4096: M=512 31.7 -> 30.6 us, M=1024 66.6 ->
+  // 60.6; with 64-row tiles it was 2 % slower, so those keep s_barrier).
+  // The arrival and the polls are LDS instructions in asm: as built-ins the
+  // compiler cannot tell them from the activation copies in flight and waits
+  // for those first.  The poll is bounded (~0.3 s), so a wave always leaves.
+  auto parity_barrier = [&](int j) {
+    const uint32_t pa = (uint32_t)(size_t)((__attribute__((address_space(3))) unsigned*)&parity_arrivals[kh]);
+    if (lane == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(pa), "v"(1u) : "memory");
+    const unsigned target = 4u * (unsigned)(j + 1);
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      unsigned c;
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(c) : "v"(pa) : "memory");
+      if (__builtin_amdgcn_readfirstlane(c) >= target) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
   auto step = [&](int j, int b, v4u& wn, uint32_t& hn, const v4i (&bc0)[kNT], const v4i (&bc1)[kNT],
                   v4i (&bn0)[kNT], v4i (&bn1)[kNT]) {
     // every wave's copy of step j has landed and its earlier LDS reads are
     // done; then the buffer of step j-1 is free for the copy of step j+2
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kNewerLoads));
-    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (BM == 128)
+      parity_barrier(j);
+    else
+      __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     __builtin_amdgcn_sched_barrier(0);
     copy_a(min(j + 2, KJ - 1), b == 0 ? 2 : b - 1);
