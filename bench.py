@@ -296,7 +296,10 @@ def read_floor(torch, bw, bufs, n: int):
 def ceilings(torch, bw, st):
     """What this GPU reaches in the same process, beside which every number
     is reported: the plain read of the step's own rotating weight copies, a
-    1 GiB read, a 512 MiB device copy and the empty-launch floor."""
+    1 GiB read, a 512 MiB device copy, the empty-launch floor, and the
+    decode step alone (code-pair lookups in an LDS table with nothing else in
+    the loop, best over launch shapes), given as the time the step's codes
+    would take at that rate."""
     out = {}
     nb = st.w.packed_bytes
     us, shape = read_floor(torch, bw, st.packed, max(200, st.R))
@@ -339,6 +342,24 @@ def ceilings(torch, bw, st):
     torch.cuda.empty_cache()
     ms, _ = graph_time(torch, lambda i: bw.probe_empty(), 1000, reps=3)
     out["empty_launch_us"] = round(ms * 1e3, 3)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = None
+    for grid, block in ((256, 512), (256, 1024), (512, 512), (1024, 256)):
+        iters = 256
+        codes = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            codes = bw.probe_decode(sink, iters, grid, block)
+            e1.record()
+            torch.cuda.synchronize()
+            rate = codes / (e0.elapsed_time(e1) * 1e-3)
+            if best is None or rate > best[0]:
+                best = (rate, grid, block)
+    step_codes = st.w.N * st.w.K // 4
+    out["decode_alone"] = {"codes_per_s": round(best[0], -6), "shape": {"grid": best[1], "block": best[2]},
+                           "step_codes": step_codes, "us_for_step_codes": round(step_codes / best[0] * 1e6, 3)}
     return out
 
 
@@ -547,6 +568,8 @@ def main():
     out["ceilings"] = ceilings(torch, bw, st)
     rs = out["ceilings"]["read_same_bytes"]["us"]
     out["roofline"]["vs_read_same_bytes"] = round(rs / (step_ms * 1e3), 4)
+    out["roofline"]["vs_decode_alone"] = round(out["ceilings"]["decode_alone"]["us_for_step_codes"]
+                                               / (step_ms * 1e3), 4)
     del st
     torch.cuda.empty_cache()
 

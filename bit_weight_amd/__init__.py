@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
                 "sherry_gemm_noalloc": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], ci),
                 "sherry_probe_read": ([vp, sz, vp, ci, ci, ci, vp], ci),
                 "sherry_probe_empty": ([vp], ci),
+                "sherry_probe_decode": ([ci, vp, ci, ci, vp], ci),
+                "sherry_probe_decode_codes": ([ci, ci, ci], i64),
             }
             for name, (args, res) in sigs.items():
                 fn = getattr(L, name)
@@ -296,6 +298,15 @@ def probe_empty(device=None) -> None:
     """Diagnostic: one empty kernel launch on the current stream."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
     _check(lib().sherry_probe_empty(_stream(dev)), "sherry_probe_empty")
+
+
+def probe_decode(sink: torch.Tensor, iters: int, grid: int, block: int) -> int:
+    """Diagnostic: one launch of the decode step alone (code-pair lookups in
+    an LDS table, nothing else); returns the number of codes it decodes.
+    `sink` is a device int32 tensor."""
+    _check(lib().sherry_probe_decode(iters, sink.data_ptr(), grid, block, _stream(sink.device)),
+           "sherry_probe_decode")
+    return int(lib().sherry_probe_decode_codes(iters, grid, block))
 
 
 def linear_scratch_bytes(M: int, N: int, K: int) -> int:

@@ -1,7 +1,10 @@
 // Measurement probes for the benchmark's ceilings, not part of the product:
 // a plain streaming read of a device buffer (the HBM read rate a kernel
 // that only loads can reach on this GPU, at the same bytes per launch as a
-// product) and an empty launch (the floor one dispatch costs back to back).
+// product), an empty launch (the floor one dispatch costs back to back) and
+// the decode step alone (the rate at which code pairs can be looked up in
+// an LDS pair table, as the matrix-core kernels decode, with nothing else
+// in the loop).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,6 +39,47 @@ __global__ __launch_bounds__(1024) void probe_read_kernel(const v4u* __restrict_
 
 __global__ void probe_empty_kernel() {}
 
+__device__ __forceinline__ uint32_t mix(uint32_t v) {
+  v ^= v >> 16;
+  v *= 0x7FEB352Du;
+  v ^= v >> 15;
+  v *= 0x846CA68Bu;
+  v ^= v >> 16;
+  return v;
+}
+
+// Every thread holds kGroups 20-bit code groups (4 codes each) and, `iters`
+// times, looks each one up as two code pairs in a 1024-entry table of 8-byte
+// entries in LDS (two lookups and four VALU address operations per group,
+// as in the product kernels) and folds the entries with XOR.  The groups are
+// made opaque to the compiler on every trip by an empty asm statement (no
+// instruction), so no lookup is hoisted or merged.  The table holds mixed
+// bits, not decoded weights: the rate does not depend on the contents.
+constexpr int kDecodeGroups = 16;
+__global__ __launch_bounds__(1024) void probe_decode_kernel(int iters, unsigned int seed, unsigned int* sink) {
+  __shared__ __attribute__((aligned(16))) uint2 tbl[1024];
+  for (int i = threadIdx.x; i < 1024; i += blockDim.x) tbl[i] = make_uint2(mix(i ^ seed), mix(i + seed));
+  __syncthreads();
+  uint32_t w[kDecodeGroups];
+#pragma unroll
+  for (int j = 0; j < kDecodeGroups; ++j)
+    w[j] = mix(seed ^ (threadIdx.x * 7919u + blockIdx.x * 104729u + j * 15485863u)) & 0xFFFFFu;
+  const uint8_t* t = reinterpret_cast<const uint8_t*>(tbl);
+  uint32_t a0 = 0, a1 = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kDecodeGroups; ++j) asm volatile("" : "+v"(w[j]));
+#pragma unroll
+    for (int j = 0; j < kDecodeGroups; ++j) {
+      const uint2 e0 = *reinterpret_cast<const uint2*>(t + ((w[j] << 3) & 0x1FF8u));
+      const uint2 e1 = *reinterpret_cast<const uint2*>(t + ((w[j] >> 7) & 0x1FF8u));
+      a0 ^= e0.x ^ e1.x;
+      a1 ^= e0.y ^ e1.y;
+    }
+  }
+  if ((a0 ^ a1) == 0x9E3779B9u) sink[0] = a0;
+}
+
 template <int U>
 hipError_t launch_read(const void* src, size_t bytes, void* sink, int grid, int block, hipStream_t s) {
   hipLaunchKernelGGL(probe_read_kernel<U>, dim3(grid), dim3(block), 0, s, static_cast<const v4u*>(src),
@@ -65,6 +109,22 @@ sherry_status sherry_probe_read(const void* src, size_t bytes, void* sink, int g
     default: return SHERRY_ERR_SHAPE;
   }
   return e == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+}
+
+sherry_status sherry_probe_decode(int iters, void* sink, int grid, int block, void* stream) {
+  if (!sink) return SHERRY_ERR_NULL;
+  if (iters < 1 || iters > (1 << 20) || grid < 1 || grid > (1 << 20) || block < 64 || block > 1024 ||
+      block % 64 != 0)
+    return SHERRY_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return SHERRY_ERR_ALIGN;
+  hipLaunchKernelGGL(probe_decode_kernel, dim3(grid), dim3(block), 0, static_cast<hipStream_t>(stream), iters,
+                     0x2545F491u, static_cast<unsigned int*>(sink));
+  return hipGetLastError() == hipSuccess ? SHERRY_OK : SHERRY_ERR_HIP;
+}
+
+int64_t sherry_probe_decode_codes(int iters, int grid, int block) {
+  if (iters < 1 || grid < 1 || block < 1) return 0;
+  return (int64_t)iters * grid * block * kDecodeGroups * 4;
 }
 
 sherry_status sherry_probe_empty(void* stream) {

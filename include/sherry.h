@@ -270,8 +270,8 @@ sherry_status sherry_gemm_plan_override(int path, int rw, int ch, int splits);
 
 /* --- Diagnostics (not part of the product) -------------------------------
  * Ceilings for the benchmark, measured in the same process as the product:
- * the plain streaming-read rate of a device buffer and the cost of an empty
- * launch. */
+ * the plain streaming-read rate of a device buffer, the cost of an empty
+ * launch and the rate of the decode step alone. */
 
 /* Reads `bytes` (a multiple of 16) of device memory at `src` (16-byte
  * aligned) with 16-byte loads: grid x block threads (block a multiple of 64,
@@ -284,6 +284,19 @@ sherry_status sherry_probe_read(const void* src, size_t bytes, void* sink, int g
 
 /* Enqueues an empty kernel (one workgroup of 64 threads) on `stream`. */
 sherry_status sherry_probe_empty(void* stream);
+
+/* The decode step of the matrix-core kernels with nothing else in the loop:
+ * grid x block threads (block a multiple of 64, at most 1024; iters and
+ * grid in [1, 2^20]) each look up sherry_probe_decode_codes(iters, 1, 1)
+ * codes as code pairs in a 1024-entry table of 8-byte entries in LDS
+ * (two 8-byte lookups per 4 codes, the product's decode).  The looked-up
+ * values are folded and written to `sink` (device, 4-byte aligned) only if
+ * they equal one fixed constant.  Asynchronous on `stream`. */
+sherry_status sherry_probe_decode(int iters, void* sink, int grid, int block, void* stream);
+
+/* Codes one sherry_probe_decode launch looks up (0 for non-positive
+ * arguments).  Host-only. */
+int64_t sherry_probe_decode_codes(int iters, int grid, int block);
 
 #ifdef __cplusplus
 }

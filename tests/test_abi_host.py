@@ -398,3 +398,23 @@ def test_noalloc_rejects_shapes_beyond_its_static_scratch():
         assert _noalloc(M=16, N=65536, K=256) not in (WS, SHAPE, ALIGN, NULL)
     finally:
         bw.plan_override()
+
+
+# ------------------------------------------------ diagnostics (host checks)
+def test_probe_argument_errors():
+    """The benchmark's probes reject bad arguments before any HIP call."""
+    L = bw.lib()
+    assert L.sherry_probe_read(None, 1024, FAKE, 256, 256, 4, None) == NULL
+    assert L.sherry_probe_read(FAKE, 1024, None, 256, 256, 4, None) == NULL
+    for nbytes, grid, block, unroll in ((0, 256, 256, 4), (1000, 256, 256, 4), (1024, 0, 256, 4),
+                                        (1024, 256, 100, 4), (1024, 256, 2048, 4), (1024, 256, 256, 3)):
+        assert L.sherry_probe_read(FAKE, nbytes, FAKE, grid, block, unroll, None) == SHAPE
+    assert L.sherry_probe_read(FAKE + 4, 1024, FAKE, 256, 256, 4, None) == ALIGN
+    assert L.sherry_probe_decode(16, None, 256, 256, None) == NULL
+    for iters, grid, block in ((0, 256, 256), ((1 << 20) + 1, 256, 256), (16, 0, 256), (16, 256, 96),
+                               (16, 256, 2048)):
+        assert L.sherry_probe_decode(iters, FAKE, grid, block, None) == SHAPE
+    assert L.sherry_probe_decode(16, FAKE + 2, 256, 256, None) == ALIGN
+    # 16 groups of 4 codes per thread and trip
+    assert L.sherry_probe_decode_codes(256, 256, 1024) == 256 * 256 * 1024 * 16 * 4
+    assert L.sherry_probe_decode_codes(0, 256, 1024) == 0
