@@ -53,19 +53,28 @@ std::atomic<int> g_ovr_path{-1}, g_ovr_rw{0}, g_ovr_ch{0}, g_ovr_splits{0};
 
 // Small-M path: decode + int8 MFMA GEMV.  One row tile per workgroup and
 // KW waves taking turns over its k-tiles.  With >= 128 row tiles, 8 waves
-// per row tile and no K-split already keep >= 1024 waves streaming; smaller
-// N uses 4 waves per row tile and splits K until there are >= 1024 waves and
-// each wave has at most ~3 k-tiles (measured on MI355X at the LLaMA shapes).
+// per row tile and no K-split already keep >= 1024 waves streaming.  With
+// fewer, up to 8 tokens use 4 waves per row tile and split K until there are
+// >= 1024 waves and each wave has at most ~3 k-tiles; above 8 tokens (whole
+// blocks of 16) the 64-bit cells of every split cost more than idle CUs
+// save, so 8 waves per row tile and K-splits only to bring a wave to ~3
+// k-tiles (measured on MI355X, kernel us, earlier rule -> this one:
+// M=16 at N=K=4096 6.40 -> 5.86, M=64 there 13.9 -> 11.1, M=16 at N=4096,
+// K=11008 9.16 -> 7.35; at M <= 8 the earlier rule was the best measured).
 GemmPlan mfma_gemv_plan_of(int M, int N, int K, int kw, int splits);
 
 GemmPlan plan_mfma_gemv(int M, int N, int K) {
   const int KT = k_tiles(K), RT = row_tiles(N);
   const int ovr_kw = g_ovr_rw.load();
-  int kw = ovr_kw == 4 || ovr_kw == 8 || ovr_kw == 16 ? ovr_kw : (RT >= 128 ? 8 : 4);
+  const bool ovr_has_kw = ovr_kw == 4 || ovr_kw == 8 || ovr_kw == 16;
+  int kw = ovr_has_kw ? ovr_kw : (RT >= 128 || M > 8 ? 8 : 4);
   if (M > 16 && kw > 8) kw = 8;   // several token blocks: at most 8 waves
   int splits = 1;
   if (g_ovr_splits.load() > 0) {
     splits = g_ovr_splits.load();
+  } else if (RT < 128 && M > 8) {
+    splits = (2 * KT + 3 * kw) / (6 * kw);   // KT / (3 kw), rounded
+    if (splits < 1) splits = 1;
   } else if (RT < 128) {
     const int by_waves = (1024 + RT * kw - 1) / (RT * kw);
     const int by_depth = (KT + 3 * kw - 1) / (3 * kw);

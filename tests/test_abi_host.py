@@ -286,7 +286,7 @@ def test_linear_scratch_and_validation():
     assert L.sherry_linear(*args(N=98)) == SHAPE
     assert L.sherry_linear(*args(x=FAKE + 4)) == ALIGN
     assert L.sherry_linear(*args(p=FAKE + 8)) == ALIGN
-    M, N, K = 16, 4096, 4096
+    M, N, K = 8, 4096, 4096            # unfused (M > 4) and split along K
     need_ws, need_sc = bw.workspace_bytes(M, N, K), bw.linear_scratch_bytes(M, N, K)
     assert need_ws > 0 and need_sc > 0
     assert L.sherry_linear(*args(M=M, N=N, K=K, ws=None)) == WS
