@@ -72,10 +72,20 @@ GemmPlan plan_mfma_gemv(int M, int N, int K) {
   int splits = 1;
   if (g_ovr_splits.load() > 0) {
     splits = g_ovr_splits.load();
-  } else if (RT < 128 && M > 8) {
+  } else if (RT >= 128) {
+    // long K, one token block: split until a wave has at most 8 k-tiles (the
+    // straight-line form's limit), 16 above 8 tokens, where each split's
+    // cells cost more (measured at N=8192, K=28672: M=1 16.6 -> 11.6 us,
+    // M=8 17.1 -> 12.6, M=16 20.3 -> 14.7; at K <= 8192 no split stays the
+    // best).  Several token blocks keep one split (unmeasured at long K).
+    if (M <= 16) {
+      const int per_split = kw * (M > 8 ? 16 : 8);
+      splits = (KT + per_split - 1) / per_split;
+    }
+  } else if (M > 8) {
     splits = (2 * KT + 3 * kw) / (6 * kw);   // KT / (3 kw), rounded
     if (splits < 1) splits = 1;
-  } else if (RT < 128) {
+  } else {
     const int by_waves = (1024 + RT * kw - 1) / (RT * kw);
     const int by_depth = (KT + 3 * kw - 1) / (3 * kw);
     splits = by_waves > by_depth ? by_waves : by_depth;
