@@ -513,6 +513,40 @@ def test_random_shapes_every_path(orc, M, N, K):
         assert_y_close(gy2.cpu().numpy(), y)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 8192, 28672), (8, 8192, 28672), (16, 8192, 28672),
+                                   (9, 4096, 4096), (16, 4096, 11008), (64, 4096, 4096),
+                                   (128, 4096, 4096)])
+def test_gemm_gemv_plan_rule_shapes(orc, M, N, K):
+    """The GEMV plans the built-in rule picks at these shapes: K split at
+    wide N and long K for one token block (a wave keeps at most 8 or 16
+    k-tiles), and 8 waves per row tile with few splits above 8 tokens at
+    narrow N (one split at K=4096, 64-token launches at M=128): y and the
+    int32 sums against the oracle."""
+    W = synth.weights(N, K, 0.02, False, seed=9300 + N + K)
+    x = synth.activations(M, K, seed=9400 + M + K)
+    T, alpha = orc.quantize(W.numpy())
+    q, s = orc.act_quant(x.numpy())
+    acc, y = orc.gemm(q, s, T, alpha, parallel=True)
+    packed, galpha = gpu_pack(W)
+    gq, gs = bw.quantize_act(x.cuda())
+    p = bw.plan(M, N, K)
+    _say(f"plan rule M={M} N={N} K={K}: {p}")
+    assert p["path"] == "decode_mfma_gemv"
+    KT, RT = -(-K // 128), -(-N // 64)
+    if RT >= 128 and M <= 16:
+        per_wave = -(-(-(-KT // p["splits"])) // (p["block"] // 64))
+        assert p["splits"] > 1 and per_wave <= (16 if M > 8 else 8), p
+    if RT < 128 and M > 8:
+        assert p["block"] == 512, p
+    ws = torch.zeros(max(bw.workspace_bytes(M, N, K), 256), dtype=torch.uint8, device="cuda")
+    gy = bw.gemm(gq, gs, packed, galpha, N, K, workspace=ws)
+    gacc = bw.gemm_i32(gq, packed, N, K, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(gacc.cpu().numpy(), acc)
+    assert_y_close(gy.cpu().numpy(), y)
+    assert int(ws.count_nonzero()) == 0          # every split's cells left zero
+
+
 # ------------------------------------------------------- HIP graph capture
 @pytest.mark.parametrize("path,M,N,K", [(None, 1, 4096, 4096),        # fused step, K-split cells
                                         (None, 8, 1024, 2048),        # quantizer + GEMV
