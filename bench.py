@@ -138,14 +138,21 @@ class Setup:
                        self.alpha[r], self.w.N, self.w.K, out=self.y, workspace=self.ws)
 
 
-def graph_time(torch, fn, n: int, reps: int = 1):
-    """Capture n calls of fn(i) into one graph; return (ms per call, graph)."""
+def graph_time(torch, fn, n: int, reps: int = 1, warm_s: float = 0.03):
+    """Capture n calls of fn(i) into one graph; return (ms per call, graph).
+    Untimed replays for about warm_s seconds come first: the first uploads
+    the graph, and the rest bring the clocks back up after the idle time of
+    the capture (the GPU's clocks drop when it idles and rise under load)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(n):
             fn(i)
-    g.replay()                       # first replay uploads the graph (untimed)
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warm_s:
+            break
     best = None
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -493,27 +500,29 @@ def main():
     # correctness of graph replay against eager (replayed several times)
     ref = st.gemm(bw, 0).clone()
     torch.cuda.synchronize()
-    # the same step replayed for ~0.2 s first, untimed: the GPU's clocks rise
-    # under sustained load, and without this the timed steps would land on
-    # the ramp (a cold start measured up to ~15 % slower than the same graph
-    # later in the run)
+    # The warmup and timed steps are captured first (each replayed once, to
+    # upload it), then the same step is replayed for ~0.2 s, untimed, and the
+    # warmup and timed steps follow at once: the GPU's clocks rise under
+    # sustained load and drop while it idles (a cold start, or one after the
+    # host-side capture of a 1000-launch graph, measured up to ~15 % slower
+    # than the same graph later in the run).
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for i in range(args.warmup):
+            st.gemm(bw, i)
+    gt = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gt):
+        for i in range(args.steps):
+            st.gemm(bw, i)
+    gw.replay()
+    gt.replay()
+    torch.cuda.synchronize()
     warm_start = time.perf_counter()
     _, gclk = graph_time(torch, lambda i: st.gemm(bw, i), max(200, st.R))
     while time.perf_counter() - warm_start < 0.2:
         gclk.replay()
         torch.cuda.synchronize()
-    del gclk
-    # warmup steps, then the timed steps
-    gw = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gw):
-        for i in range(args.warmup):
-            st.gemm(bw, i)
     gw.replay()
-    torch.cuda.synchronize()
-    gt = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gt):
-        for i in range(args.steps):
-            st.gemm(bw, i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
