@@ -10,9 +10,11 @@
 //    one row per lane) times KW waves that share a row tile and take turns
 //    over its k-tiles.  It covers the k-tiles of one K-split in stages of CH
 //    k-tiles (128 inputs each); the tables of one stage live in LDS.
-//  * Each lane streams its codes, 16 + 4 bytes per k-tile, both loads
-//    coalesced across the wave; the next stage's codes are requested before
-//    the current stage's lookups.
+//  * Each lane streams one slot of the tile, 16 + 4 bytes per k-tile, both
+//    loads coalesced across the wave; the next stage's codes are requested
+//    before the current stage's lookups.  Two 4 x 4 lane transposes then
+//    give each lane its own row's 32 codes (the format stores them in four
+//    slots, as the matrix-core kernels consume them).
 //  * Table layout: dword [segment][token pair][code], 32 codes per table
 //    (128 bytes).  Entry 2p holds the pattern-p dot products of two tokens as
 //    two int16 halves; entry 2p+1 holds their negations, so the code's sign
@@ -191,9 +193,11 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
 #pragma unroll
           for (int pp = 0; pp < MP; ++pp) h[pp] = short2_t{0, 0};
           const uint32_t* lc = lut + c * (32 * MP * 32);
+          uint32_t glo[4], ghb;   // this lane's row: its four code groups
+          row_groups(cur[i], lane, glo, ghb);
 #pragma unroll
           for (int j = 0; j < 32; ++j) {
-            const uint32_t code = code_at(cur[i], j);
+            const uint32_t code = group_code(glo[j >> 3], ghb >> (8 * (j >> 3)), j & 7);
 #pragma unroll
             for (int pp = 0; pp < MP; ++pp)
               h[pp] += __builtin_bit_cast(short2_t, lc[(j * MP + pp) * 32 + code]);

@@ -24,14 +24,12 @@
 //    j+2 starts right after the barrier of step j, once every wave is done
 //    with the buffer it overwrites, and has two steps to land;
 //  * weights: each wave decodes exactly the B operands it consumes.  It loads
-//    its row tile's 1280-byte k-tile coalesced (lane r = tile row r, 16 + 4
-//    bytes) and moves dwords g and g+1 of rows 16t..16t+15 to lane group g of
-//    column block t with two 4 x 4 transposes of 16-lane rows
-//    (v_permlane32_swap, then v_permlane16_swap).  Lane l of a block then
-//    holds weight row l%16 and, for lane group g = l/16, codes 8g..8g+7 of
+//    its row tile's 1280-byte k-tile coalesced (lane l = slot l, 16 + 4
+//    bytes), which by the format's design already holds, for column block t,
+//    weight row 16t + l%16 and, for lane group g = l/16, codes 8g..8g+7 of
 //    the k-tile (inputs 32g..32g+31: the first half in MFMA sub-step 0, the
-//    second in sub-step 1); the A operands use the same input order, which a
-//    dot product does not see.  A 1024-entry LDS table maps a 10-bit code
+//    second in sub-step 1): dword t and byte t of the slot's last dword.  The
+//    A operands use the same input order, which a dot product does not see.  A 1024-entry LDS table maps a 10-bit code
 //    pair to its 8 int8 weights, so 4 codes cost two 8-byte lookups;
 //  * codes come through a buffer descriptor into two register stages used
 //    in turn; a k-step's codes are decoded (table lookups) between the
@@ -84,21 +82,6 @@ __device__ __forceinline__ int a_off(int r, int c) { return (r * 8 + (c ^ ((r >>
 
 // s_waitcnt operand: vmcnt(vm), lgkmcnt(0), expcnt not waited.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 0x70; }
-
-// 4 x 4 transpose of 16-lane rows: out[t] row g = in[g] row t.
-__device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
-                                           uint32_t (&out)[4]) {
-  // swap the upper 32 lanes of the first operand with the lower 32 of the second
-  const auto s02 = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
-  const auto s13 = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
-  // swap the odd 16-lane rows of the first operand with the even rows of the second
-  const auto t01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
-  const auto t23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
-  out[0] = t01[0];
-  out[1] = t01[1];
-  out[2] = t23[0];
-  out[3] = t23[1];
-}
 
 // B operands of one column block and sub-step: 4 codes (20 bits of v) as
 // two code pairs, one 8-byte table entry each.
@@ -232,7 +215,6 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
       buffer_rsrc(a.packed + tile_offset(rt, 0, KT), (size_t)KT * kTileBytes);
   const __amdgpu_buffer_rsrc_t ra =
       buffer_rsrc(a.x + (size_t)m0 * K, (size_t)(M - m0) * (size_t)K);
-  const uint32_t sh = 8u * (uint32_t)g;  // bit 40g mod 32
 
   // activations: the 4 waves of a parity copy its k-tile, BM rows x 128
   // bytes; copy jj of wave `wave` fills rows (BM/4) wave + 8 jj .. +7, lane
@@ -285,17 +267,21 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   };
   const uint8_t* d2 = reinterpret_cast<const uint8_t*>(dec2);
   // the 20-bit code groups of one register stage: lane (l16, g) of block t
-  // gets dwords g (lo) and g+1 (hi) of row 16t+l16, i.e. codes 8g..8g+3
-  // (sub-step 0) and 8g+4..8g+7 (sub-step 1)
+  // holds codes 8g..8g+3 of row 16t+l16 (sub-step 0) in the low 20 bits of
+  // dword t, and codes 8g+4..8g+7 (sub-step 1) in its top 12 bits and byte t
+  // of h.  The empty asm statements make the compiler form both halves here,
+  // in registers of their own: left to itself it reads f0 out of the stage
+  // registers and forms f1 late, so the code load into the stage that
+  // follows gets fresh registers and the loop's back edge copies them back
+  // after waiting for every load (measured at N=14336, K=4096: M=128 22.9
+  // against 20.5 us with them).
   auto split = [&](const v4u& w, uint32_t h, uint32_t (&f0)[kNT], uint32_t (&f1)[kNT]) {
-    uint32_t lo[kNT], hi[kNT];
-    transpose4(w.x, w.y, w.z, w.w, lo);
-    transpose4(w.y, w.z, w.w, h, hi);
+    const uint32_t wt[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-      const uint32_t x0 = __builtin_amdgcn_alignbit(hi[t], lo[t], sh);
-      f0[t] = x0;
-      f1[t] = __builtin_amdgcn_alignbit(hi[t] >> sh, x0, 20);
+      f0[t] = wt[t];
+      f1[t] = __builtin_amdgcn_alignbit(h >> (8 * t), wt[t], 20);
+      asm volatile("" : "+v"(f0[t]), "+v"(f1[t]));
     }
   };
   // Step j (activation buffer b = j % 3): its B operands bc0 / bc1 were

@@ -32,31 +32,39 @@ __device__ __forceinline__ uint32_t encode_block(float w0, float w1, float w2, f
   return 2u * p + f;
 }
 
-// One wave per format tile: lane r encodes the 32 blocks of tile row r and
-// writes its 16 + 4 bytes (both stores coalesced across the wave).  Rows
-// past N and blocks past K (padding) get code 0 and read nothing.
+// One wave per format tile.  Lane L = 16g + i encodes the 8 blocks
+// 8g..8g+7 of the tile rows 16t + i (t = 0..3) and writes each 40-bit group:
+// its low 32 bits as dword t of the lane's 16 bytes, its high 8 bits as byte
+// t of the lane's 4 bytes (both stores coalesced across the wave).  Rows past
+// N and blocks past K (padding) get code 0 and read nothing.
 __global__ __launch_bounds__(64) void pack_codes_kernel(const float* __restrict__ W,
                                                         uint8_t* __restrict__ packed,
                                                         int N, int K) {
   const int KT = k_tiles(K);
   const int rt = blockIdx.x / KT, kt = blockIdx.x % KT;
   const int lane = threadIdx.x;
-  const int n = rt * kTileRows + lane;
-  const int nb = n < N ? min(32, (K - kt * kTileK) / 4) : 0;   // real blocks of this row
-  const float4* src = reinterpret_cast<const float4*>(W + (size_t)min(n, N - 1) * K + (size_t)kt * kTileK);
-  uint32_t w[5] = {0, 0, 0, 0, 0};
+  const int i = lane & 15, g = lane >> 4;
+  const int kb = min(32, (K - kt * kTileK) / 4);   // real blocks of the tile's rows
+  uint32_t lo[4], hi = 0;
 #pragma unroll
-  for (int b = 0; b < 32; ++b) {
-    if (b >= nb) continue;
-    const float4 v = src[b];
-    const uint32_t c = encode_block(v.x, v.y, v.z, v.w);
-    const int bit = 5 * b, d = bit >> 5, sh = bit & 31;
-    w[d] |= c << sh;
-    if (sh > 27) w[d + 1] |= c >> (32 - sh);
+  for (int t = 0; t < 4; ++t) {
+    const int n = rt * kTileRows + 16 * t + i;
+    const int nb = n < N ? kb : 0;
+    const float4* src = reinterpret_cast<const float4*>(W + (size_t)min(n, N - 1) * K + (size_t)kt * kTileK);
+    uint64_t v = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int b = 8 * g + j;
+      if (b >= nb) continue;
+      const float4 x = src[b];
+      v |= (uint64_t)encode_block(x.x, x.y, x.z, x.w) << (5 * j);
+    }
+    lo[t] = (uint32_t)v;
+    hi |= (uint32_t)(v >> 32) << (8 * t);
   }
   uint8_t* tile = packed + tile_offset(rt, kt, KT);
-  *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
-  *reinterpret_cast<uint32_t*>(tile + kTileHiOff + 4 * lane) = w[4];
+  *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  *reinterpret_cast<uint32_t*>(tile + kTileHiOff + 4 * lane) = hi;
 }
 
 // The same ternarization written in the 2-bit baseline format: one wave per

@@ -1,8 +1,13 @@
 // Device-side definitions shared by the gfx950 kernels of libsherry.
 //
 // Format (see include/sherry.h): 5-bit code c = 2*p + s per 4-weight block;
-// tiles of 64 rows x 128 columns, 1280 bytes, row-tile-major; a row's 32
-// codes in a tile are a 160-bit little-endian string split 16 + 4 bytes.
+// tiles of 64 rows x 128 columns, 1280 bytes, row-tile-major.  Tile row
+// r = 16t + i keeps its 32 codes as four 40-bit groups (group g = blocks
+// 8g..8g+7); the group belongs to slot L = 16g + i, which holds its low 32
+// bits as dword t of 16 bytes at 16L and its high 8 bits as byte t of the
+// dword at 1024 + 4L.  A wave loading slot L per lane (16 + 4 bytes) thus
+// holds in lane (i, g) block g's group of rows i, 16 + i, 32 + i, 48 + i:
+// the operand layout of the matrix-core kernels, with no lane exchange.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,7 +18,7 @@ namespace sherry {
 constexpr int kTileRows = 64;     // rows per format tile (one per wave lane)
 constexpr int kTileK = 128;       // weights per row per tile (32 blocks)
 constexpr int kTileBytes = 1280;  // 64 rows * 32 codes * 5 bits / 8
-constexpr int kTileHiOff = 1024;  // byte offset of the 4-byte code parts
+constexpr int kTileHiOff = 1024;  // byte offset of the groups' high bytes
 
 // Tiles of an [N,K] matrix: padded to whole 64-row x 128-column tiles whose
 // extra blocks hold code 0 and are never used by a product.
@@ -73,12 +78,48 @@ __host__ __device__ constexpr uint32_t code2_word(uint32_t b) {
   return w;
 }
 
-// 5-bit code j (0..31) of a row's 160-bit string held in w[0..4].  Called
-// with a compile-time j inside unrolled loops, so the branch folds away.
-__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[5], int j) {
-  const int bit = 5 * j, d = bit >> 5, sh = bit & 31;
-  if (sh <= 27) return (w[d] >> sh) & 31u;
-  return __builtin_amdgcn_alignbit(w[d + 1], w[d], sh) & 31u;
+// 4 x 4 transpose of 16-lane rows: out[t] row g = in[g] row t.
+__device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                           uint32_t (&out)[4]) {
+  // swap the upper 32 lanes of the first operand with the lower 32 of the second
+  const auto s02 = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+  // swap the odd 16-lane rows of the first operand with the even rows of the second
+  const auto t01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  const auto t23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  out[0] = t01[0];
+  out[1] = t01[1];
+  out[2] = t23[0];
+  out[3] = t23[1];
+}
+
+// From a wave's slot loads (lane L: the 16 bytes at 16L in w[0..3], the
+// dword at 1024 + 4L in w[4]) to one tile row per lane: lane r = 16t + i
+// gets row r's four code groups, the low 32 bits of group g in lo[g] and
+// its high 8 bits in byte g of hb.  Group g of row r is dword t and byte t
+// of slot 16g + i, so the transpose of the four dwords brings lane r its
+// groups' low words, and the transpose of w[4] the four dwords holding
+// their high bytes, whose byte t two byte permutes gather.
+__device__ __forceinline__ void row_groups(const uint32_t (&w)[5], int lane, uint32_t (&lo)[4],
+                                           uint32_t& hb) {
+  uint32_t hw[4];
+  transpose4(w[0], w[1], w[2], w[3], lo);
+  transpose4(w[4], w[4], w[4], w[4], hw);
+  // v_perm_b32 selector bytes: 0..3 pick bytes of the second operand, 4..7
+  // of the first, 12 gives zero
+  const uint32_t t = (uint32_t)(lane >> 4);
+  const uint32_t s01 = t | ((4u + t) << 8) | 0x0C0C0000u;
+  const uint32_t s23 = 0x00000C0Cu | (t << 16) | ((4u + t) << 24);
+  hb = __builtin_amdgcn_perm(hw[1], hw[0], s01) | __builtin_amdgcn_perm(hw[3], hw[2], s23);
+}
+
+// Code jj (0..7) of a 40-bit group held as lo (bits 0..31) and the low
+// byte of hi (bits 32..39).  Called with a compile-time jj, so the branches
+// fold.
+__device__ __forceinline__ uint32_t group_code(uint32_t lo, uint32_t hi, int jj) {
+  if (jj <= 5) return (lo >> (5 * jj)) & 31u;
+  if (jj == 6) return __builtin_amdgcn_alignbit(hi, lo, 30) & 31u;
+  return (hi >> 3) & 31u;
 }
 
 // x as read from another lane of its 16-lane row by DPP control CTRL.

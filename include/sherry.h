@@ -37,10 +37,14 @@
  *     2*r1 + r2 where z is the zero position and r1 (r2) says the 2nd (3rd)
  *     nonzero's sign differs from the 1st's; s = 1 iff the 1st nonzero is -1.
  *     Rows are grouped in tiles of 64 rows x 128 columns (1280 bytes),
- *     row-tile-major and column-tile-minor.  A row's 32 codes in a tile form
- *     a 160-bit little-endian string with code j at bits [5j, 5j+5); bits
- *     0..127 of tile row r sit at tile byte 16*r and bits 128..159 at tile
- *     byte 1024 + 4*r.  The matrix is padded to whole tiles (N up to a
+ *     row-tile-major and column-tile-minor.  Tile row r = 16t + i
+ *     (t = 0..3, i = 0..15) keeps its 32 codes as four groups of 8: group g
+ *     (blocks 8g..8g+7) is a 40-bit little-endian string with block 8g+jj at
+ *     bits [5jj, 5jj+5).  It belongs to slot L = 16g + i: group bits 0..31
+ *     are the 4 bytes at tile byte 16*L + 4*t, bits 32..39 the byte at tile
+ *     byte 1024 + 4*L + t.  (Slot L is what lane L of a 64-wide wave loads;
+ *     it holds that lane's matrix-core operands.)  The matrix is padded to
+ *     whole tiles (N up to a
  *     multiple of 64, K up to a multiple of 128); padding blocks hold code 0
  *     and no product uses them.  Total sherry_packed_bytes(N,K) =
  *     ceil(N/64) * ceil(K/128) * 1280 bytes (N*K*5/32 when no padding).

@@ -35,11 +35,13 @@
 // bit): W is [N,K] row-major, K % 4 == 0.  The matrix is padded to Np =
 // N rounded up to 64 rows and Kp = K rounded up to 128 columns; tiles of 64
 // rows x 128 columns (32 blocks per row) are stored row-tile-major,
-// column-tile minor, 1280 bytes each.  A row's 32 codes form a 160-bit
-// little-endian string, code j at bits [5j, 5j+5).  Bits 0..127 of row r
-// sit at tile byte 16*r, bits 128..159 at tile byte 1024 + 4*r.  Blocks past
-// K and rows past N hold code 0 (they carry no weights; a product never
-// uses them).  Total Np*Kp*5/32 bytes.
+// column-tile minor, 1280 bytes each.  Tile row r = 16t + i (t = 0..3,
+// i = 0..15) has its 32 codes in four groups of 8: group g (blocks
+// 8g..8g+7) is a 40-bit little-endian string, block 8g+jj at bits
+// [5jj, 5jj+5).  The group belongs to slot L = 16g + i: its bits 0..31 are
+// the 4 bytes at tile byte 16*L + 4*t, its bits 32..39 the byte at tile
+// byte 1024 + 4*L + t.  Blocks past K and rows past N hold code 0 (they
+// carry no weights; a product never uses them).  Total Np*Kp*5/32 bytes.
 //
 // Build: g++ -std=c++17 -O2 -fno-fast-math -ffp-contract=off -shared -fPIC
 // (liboracle.so, single-threaded).  The same source built with -fopenmp
@@ -115,10 +117,19 @@ void tile_slot(int64_t n, int64_t b, int64_t K, int64_t* tile_base, int64_t* r,
   *j = (int)(b % 32);
 }
 
-// Byte address of bit `bit` (0..159) of row r's 160-bit string in a tile.
-int64_t bit_byte(int64_t tile_base, int64_t r, int bit) {
-  if (bit < 128) return tile_base + 16 * r + bit / 8;
-  return tile_base + 1024 + 4 * r + (bit - 128) / 8;
+// Byte address and bit position of bit k (0..4) of the code of block j
+// (0..31) of tile row r.
+void code_bit(int64_t tile_base, int64_t r, int j, int k, int64_t* byte, int* bit) {
+  const int64_t t = r / 16, i = r % 16, g = j / 8;
+  const int p = 5 * (j % 8) + k;            // bit within the 40-bit group
+  const int64_t slot = 16 * g + i;
+  if (p < 32) {
+    *byte = tile_base + 16 * slot + 4 * t + p / 8;
+    *bit = p % 8;
+  } else {
+    *byte = tile_base + 1024 + 4 * slot + t;
+    *bit = p - 32;
+  }
 }
 
 }  // namespace
@@ -198,9 +209,9 @@ int oracle_pack(const int8_t* T, int64_t N, int64_t K, uint8_t* packed) {
       tile_slot(n, b, K, &base, &r, &j);
       for (int i = 0; i < 5; ++i) {
         if ((c >> i) & 1) {
-          const int bit = 5 * j + i;
-          int64_t a = bit_byte(base, r, bit);
-          const int within = (bit < 128 ? bit : bit - 128) % 8;
+          int64_t a;
+          int within;
+          code_bit(base, r, j, i, &a, &within);
           packed[a] |= (uint8_t)(1u << within);
         }
       }
@@ -219,9 +230,9 @@ int oracle_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* T) {
       tile_slot(n, b, K, &base, &r, &j);
       int c = 0;
       for (int i = 0; i < 5; ++i) {
-        const int bit = 5 * j + i;
-        int64_t a = bit_byte(base, r, bit);
-        const int within = (bit < 128 ? bit : bit - 128) % 8;
+        int64_t a;
+        int within;
+        code_bit(base, r, j, i, &a, &within);
         c |= ((packed[a] >> within) & 1) << i;
       }
       int v[4];
