@@ -8,10 +8,12 @@
 //
 // Workgroup tile: BM = 128 activation rows x BN = 256 weight rows (4 format
 // row tiles), k-steps of one format k-tile (128 inputs); 8 waves, two per
-// SIMD: wave (kh, w) takes the k-tiles of parity kh (2j + kh) of row tile w,
+// SIMD: wave (kh, w) takes the k-tiles of phase kh (2j + kh) of row tile w,
 // i.e. 64 weight rows = 4 MFMA column blocks, against all 128 activation
-// rows = 8 MFMA row blocks (8 x 4 accumulators); the two parities' sums are
-// added in the epilogue.
+// rows = 8 MFMA row blocks (8 x 4 accumulators); the two phases' sums are
+// added in the epilogue.  With 64-row tiles on a small grid the 8 waves
+// split instead into 2 row tiles x KP = 4 k-phases (BN = 128, k-tiles
+// 4j + kh): twice the workgroups, each a quarter of K per wave.
 // A decoded weight operand therefore feeds 8 MFMAs and an activation
 // fragment 4, which keeps the LDS work per k-tile (pair-table lookups plus
 // activation fragments) well below the matrix-core time.
@@ -20,7 +22,7 @@
 //    (no registers on the way), 8 lanes per 128-byte row so every load reads
 //    whole lines; rows sit in a row-major tile whose 16-byte chunks are
 //    XOR-swizzled (see a_off) so the MFMA A reads (16 rows, one chunk) hit 16
-//    different bank groups.  Three buffers per parity: the copy for k-step
+//    different bank groups.  Three buffers per phase: the copy for k-step
 //    j+2 starts right after the barrier of step j, once every wave is done
 //    with the buffer it overwrites, and has two steps to land;
 //  * weights: each wave decodes exactly the B operands it consumes.  It loads
@@ -50,23 +52,26 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kBN = 256;                        // workgroup tile width (weight rows)
 constexpr int kNT = kTileRows / 16;             // 4 column blocks per wave (one row tile)
 constexpr int kBK = kTileK;                     // 128
-constexpr int kABufs = 3;                       // activation buffers per parity
-constexpr int kThreads = 512;                   // 4 row tiles x 2 k-tile parities
-constexpr int kOutLd = kBN + 16;                // words per row of the epilogue tiles (the 4
-                                                // row groups of an MFMA block hit 4 bank quarters)
-constexpr int kLdsOut = 2 * 32 * kOutLd * 4;    // epilogue tiles (32 rows, both parities)
+constexpr int kABufs = 3;                       // activation buffers per k-phase
+constexpr int kThreads = 512;                   // 8 waves: row tiles x k-phases
 
-// The sizes that follow from the tile height BM (128 or 64 activation rows).
-template <int BM>
+// The sizes that follow from the tile height BM (128 or 64 activation rows)
+// and the number of k-phases KP (2, or 4 with 64-row tiles).
+template <int BM, int KP>
 struct Tiling {
+  static_assert(KP == 2 || (KP == 4 && BM == 64), "k-phases: 2, or 4 with 64-row tiles");
+  static constexpr int kRT = kThreads / 64 / KP;       // row tiles per workgroup (4 or 2)
+  static constexpr int kBN = kRT * kTileRows;          // workgroup tile width (256 or 128 weight rows)
+  static constexpr int kOutLd = kBN + 16;              // words per row of the epilogue tiles (the 4
+                                                       // row groups of an MFMA block hit 4 bank quarters)
+  static constexpr int kLdsOut = KP * 32 * kOutLd * 4; // epilogue tiles (32 rows, every phase)
   static constexpr int kMT = BM / 16;                  // row blocks per wave (8 or 4)
   static constexpr int kAStage = BM * kBK;             // activation bytes per k-step
-  static constexpr int kRowsPerWave = BM / 4;          // rows each wave of a parity copies
+  static constexpr int kRowsPerWave = BM / kRT;        // rows each wave of a phase copies
   static constexpr int kACopies = kRowsPerWave / 8;    // 1 KB copies (8 rows) per wave per k-step
-  static constexpr int kLdsMain = 2 * kABufs * kAStage;  // activation buffers x parities
+  static constexpr int kLdsMain = KP * kABufs * kAStage;  // activation buffers x phases
   static constexpr int kLdsBytes = kLdsMain > kLdsOut ? kLdsMain : kLdsOut;
   // vector-memory ops a wave issues between a k-step's activation copy and
   // that step's barrier: the codes three steps ahead of it (2), the next
@@ -158,17 +163,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-template <int BM>
+template <int BM, int KP>
 __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* packed, const int8_t* x,
                                                              const float* xf, int M, int N, int K,
                                                              int n_tiles, int /*unused*/, const float* s_x,
                                                              const float* alpha, float* y, int32_t* acc_out,
                                                              int32_t* partials) {
   const GemmArgs a = product_args(packed, x, xf, M, N, K, s_x, alpha, y, acc_out, partials);
-  using T = Tiling<BM>;
+  using T = Tiling<BM, KP>;
   constexpr int kBM = BM, kMT = T::kMT, kAStage = T::kAStage, kACopies = T::kACopies;
   constexpr int kLdsBytes = T::kLdsBytes, kNewerLoads = T::kNewerLoads;
-  // the activation buffers [buffer][parity]; after the main loop the
+  constexpr int kRT = T::kRT, kBN = T::kBN, kOutLd = T::kOutLd;
+  // the activation buffers [buffer][phase]; after the main loop the
   // epilogue tile reuses them
   // (32-bit words: every view below is a character type or 32-bit lanes)
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsBytes / 4];
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   const int m0 = mt_idx * kBM, n0 = nt_idx * kBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave = wv & 3, kh = wv >> 2;            // row tile, k-tile parity
+  const int wave = wv % kRT, kh = wv / kRT;        // row tile, k-phase
   const int l16 = lane & 15, g = lane >> 4;
 
   if (tid < 2) parity_arrivals[tid] = 0u;   // published by the prologue's barrier
@@ -216,8 +222,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   const __amdgpu_buffer_rsrc_t ra =
       buffer_rsrc(a.x + (size_t)m0 * K, (size_t)(M - m0) * (size_t)K);
 
-  // activations: the 4 waves of a parity copy its k-tile, BM rows x 128
-  // bytes; copy jj of wave `wave` fills rows (BM/4) wave + 8 jj .. +7, lane
+  // activations: the kRT waves of a phase copy its k-tile, BM rows x 128
+  // bytes; copy jj of wave `wave` fills rows (BM/kRT) wave + 8 jj .. +7, lane
   // L taking chunk (L & 7) ^ swizzle of row L >> 3 (its LDS position is
   // fixed at 16 L).  Rows past M read row M-1 (they feed only unstored rows).
   int a_v[kACopies];
@@ -228,14 +234,15 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
     a_v[jj] = min(row, M - 1 - m0) * K + c * 16;
   }
   // first input of a copy's chunk in its k-step: the swizzle (row >> 1) & 7
-  // of row (BM/4) wave + 8 jj + (lane >> 3) is 4 (jj & 1) + (lane >> 4)
-  // (BM/4 is a multiple of 16)
+  // of row (BM/kRT) wave + 8 jj + (lane >> 3) is 4 (jj & 1) + (lane >> 4)
+  // (BM/kRT is a multiple of 16)
+  static_assert(T::kRowsPerWave % 16 == 0, "rows per wave: a multiple of 16");
   int a_k[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) a_k[p] = 16 * ((lane & 7) ^ (4 * p + (lane >> 4)));
   // an offset the descriptor's range check rejects (the copy writes zeros)
   const int a_oob = (size_t)(M - m0) * (size_t)K > 0x7FFFFFFFull ? 0x7FFFFFFF : (M - m0) * K;
-  auto a_buf = [&](int b) { return reinterpret_cast<int8_t*>(lds) + (b * 2 + kh) * kAStage; };
+  auto a_buf = [&](int b) { return reinterpret_cast<int8_t*>(lds) + (b * KP + kh) * kAStage; };
 
   v4i acc[kMT][kNT];
 #pragma unroll
@@ -243,17 +250,17 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-  // this wave's k-tile of pair j (2j + kh, clamped: a prefetch past the end
-  // re-reads the last k-tile)
-  const int KJ = (KT + 1) / 2;
-  auto ktile = [&](int j) { return min(2 * j + kh, KT - 1); };
+  // this wave's k-tile of step j (KP j + kh, clamped: a prefetch past the
+  // end re-reads the last k-tile)
+  const int KJ = (KT + KP - 1) / KP;
+  auto ktile = [&](int j) { return min(KP * j + kh, KT - 1); };
   // codes, coalesced (lane = tile row)
   auto load_codes = [&](int j, v4u& w, uint32_t& h) {
     const int ks = ktile(j) * kTileBytes;
     w = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, ks, 0);
     h = __builtin_amdgcn_raw_buffer_load_b32(rc, kTileHiOff + 4 * lane, ks, 0);
   };
-  // this wave's share of the activation tile of pair j into buffer b
+  // this wave's share of the activation tile of step j into buffer b
   auto copy_a = [&](int j, int b) {
     const int ka = ktile(j) * kBK;
     int8_t* dst = a_buf(b) + T::kRowsPerWave * wave * kBK;
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
     split(wn, hn, f0, f1);
     load_codes(min(j + 3, KJ - 1), wn, hn);
     __builtin_amdgcn_sched_barrier(0);
-    if (2 * j + kh < KT)     // odd KT: the last pair has one k-tile
+    if (KP * j + kh < KT)    // KT not a multiple of KP: the last step is short
       mg_mfma<true, kMT>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
     else
       mg_mfma<false, kMT>(acc, bc0, bc1, a_buf(b), l16, g, f0, f1, bn0, bn1, d2);
@@ -378,8 +385,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
   // Epilogue, 32 rows (two row blocks) at a time: every wave writes its raw
-  // int32 sums into its parity's row-major LDS tile, then each thread adds
-  // the two parities for 4 consecutive columns of one row and stores
+  // int32 sums into its phase's row-major LDS tile, then each thread adds
+  // the KP phases for 4 consecutive columns of one row and stores
   // y = ((float)acc * s_x[m]) * alpha[n] (or the int32 sum), 16 bytes per
   // lane, so each store instruction writes whole 128-byte lines, marked
   // non-temporal (the output is not read again here: measured 7 % faster at
@@ -392,9 +399,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   float4 al4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (want_y && n < N) al4 = make_float4(a.alpha[n], a.alpha[n + 1], a.alpha[n + 2], a.alpha[n + 3]);
   if (want_y && tid < kBM) sxs[tid] = a.s_x[min(m0 + tid, M - 1)];
-  int* ot0 = reinterpret_cast<int*>(lds);      // [32][kOutLd] sums of parity 0, then parity 1
-  int* ot1 = ot0 + 32 * kOutLd;
-  int* mine = kh == 0 ? ot0 : ot1;
+  int* ot = reinterpret_cast<int*>(lds);       // [phase][32][kOutLd] sums
+  int* mine = ot + kh * 32 * kOutLd;
 #pragma unroll
   for (int qq = 0; qq < kMT / 2; ++qq) {
     __syncthreads();  // the previous use of the LDS area is finished
@@ -410,9 +416,9 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
     for (int k = 0; k < 32 * (kBN / 4) / kThreads; ++k) {
       const int ml = tid / (kBN / 4) + (kThreads / (kBN / 4)) * k;   // row within the 32
       const int m = m0 + 32 * qq + ml;
-      const v4i s0 = *reinterpret_cast<const v4i*>(&ot0[ml * kOutLd + 4 * c4]);
-      const v4i s1 = *reinterpret_cast<const v4i*>(&ot1[ml * kOutLd + 4 * c4]);
-      const v4i sum = s0 + s1;
+      v4i sum = *reinterpret_cast<const v4i*>(&ot[ml * kOutLd + 4 * c4]);
+#pragma unroll
+      for (int ph = 1; ph < KP; ++ph) sum += *reinterpret_cast<const v4i*>(&ot[(ph * 32 + ml) * kOutLd + 4 * c4]);
       if (m < M && n < N) {
         if (want_y) {
           const float sx = sxs[32 * qq + ml];
@@ -427,32 +433,38 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   }
 }
 
-template <int BM>
+template <int BM, int KP>
 hipError_t launch_tiles(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  const int nt = (a.N + kBN - 1) / kBN;
-  launch_product_kernel(mfma_gemm_kernel<BM>, dim3(p.grid), dim3(kThreads), 0, stream, a, nt, 0);
+  const int nt = (a.N + Tiling<BM, KP>::kBN - 1) / Tiling<BM, KP>::kBN;
+  launch_product_kernel(mfma_gemm_kernel<BM, KP>, dim3(p.grid), dim3(kThreads), 0, stream, a, nt, 0);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int mfma_gemm_lds_bytes(int bm) {
-  return (bm == 64 ? Tiling<64>::kLdsBytes : Tiling<128>::kLdsBytes) + 1024 * 8 + bm * 4;
+int mfma_gemm_lds_bytes(int bm, int kp) {
+  const int main_bytes = bm == 128 ? Tiling<128, 2>::kLdsBytes
+                         : kp == 4 ? Tiling<64, 4>::kLdsBytes
+                                   : Tiling<64, 2>::kLdsBytes;
+  return main_bytes + 1024 * 8 + bm * 4;
 }
 
 int mfma_gemm_threads() { return kThreads; }
 
-int mfma_gemm_grid(int M, int N, int bm) {
-  const int mt = (M + bm - 1) / bm, nt = (N + kBN - 1) / kBN;
+int mfma_gemm_grid(int M, int N, int bm, int kp) {
+  const int bn = kThreads / 64 / kp * kTileRows;
+  const int mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn;
   const int per_xcd = (nt + 7) / 8;
   return 8 * per_xcd * mt;
 }
 
-// plan.rw carries the tile height in units of 64 activation rows (1 or 2).
+// plan.rw carries the tile height in units of 64 activation rows (1 or 2),
+// plan.ch the k-phases (2, or 4 with 64-row tiles).
 hipError_t launch_mfma_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  return p.rw == 1 ? launch_tiles<64>(p, a, stream)
-         : p.rw == 2 ? launch_tiles<128>(p, a, stream)
-                     : hipErrorInvalidValue;
+  if (p.rw == 1 && p.ch == 4) return launch_tiles<64, 4>(p, a, stream);
+  if (p.rw == 1 && p.ch == 2) return launch_tiles<64, 2>(p, a, stream);
+  if (p.rw == 2 && p.ch == 2) return launch_tiles<128, 2>(p, a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sherry

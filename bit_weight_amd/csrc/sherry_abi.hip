@@ -165,17 +165,26 @@ namespace {
 // with rw = 1 or 2 in the override picks the height.
 GemmPlan plan_prefill(int M, int N, int K) {
   GemmPlan p{};
-  const long long nt = (N + 255) / 256;
-  int bm = ((M + 63) / 64) * nt <= 256 ? 64 : 128;
+  const long long mt64 = (M + 63) / 64;
+  int bm = mt64 * ((N + 255) / 256) <= 256 ? 64 : 128;
   const int ovr_rw = g_ovr_rw.load();
-  if (g_ovr_path.load() == 1 && (ovr_rw == 1 || ovr_rw == 2)) bm = 64 * ovr_rw;
+  const bool forced = g_ovr_path.load() == 1;
+  if (forced && (ovr_rw == 1 || ovr_rw == 2)) bm = 64 * ovr_rw;
+  // 64-row tiles split each workgroup's K four ways when twice the
+  // workgroups still fit the GPU in one round (tiles 128 weight rows wide):
+  // measured at K=4096, M=128: N=14336 20.6 -> 14.5 us, N=4096 20.4 -> 14.2;
+  // at M=136, N=4096, K=14336 56.3 -> 36.3
+  int kp = bm == 64 && mt64 * ((N + 127) / 128) <= 256 ? 4 : 2;
+  const int ovr_ch = g_ovr_ch.load();
+  if (forced && bm == 64 && (ovr_ch == 2 || ovr_ch == 4)) kp = ovr_ch;
   p.path = 1;
   p.rw = bm / 64;
-  p.grid = mfma_gemm_grid(M, N, bm);
+  p.ch = kp;
+  p.grid = mfma_gemm_grid(M, N, bm, kp);
   p.block = mfma_gemm_threads();
   p.splits = 1;
   p.kt_per_split = k_tiles(K);
-  p.lds_bytes = mfma_gemm_lds_bytes(bm);
+  p.lds_bytes = mfma_gemm_lds_bytes(bm, kp);
   p.ws_bytes = 0;
   return p;
 }
@@ -183,18 +192,23 @@ GemmPlan plan_prefill(int M, int N, int K) {
 
 // M <= 16: the built-in small-M path (or the override's); 16 < M <= 64: the
 // matrix-core GEMV unless the prefill kernel is forced; 64 < M <= 128: the
-// same GEMV in launches of 64 tokens (each streams the weights again), except
-// above 96 tokens when the prefill's 64-row tiles number >= 96, i.e. for
-// wide N (measured at N=14336, K=4096: two GEMV launches take 19.7 us at
-// M=96 and 22.2-22.9 us at M=104-128, the 112 prefill tiles 21.2 us; at
-// N=4096 the prefill would have 32 tiles); M > 128: prefill.
+// prefill kernel, except at M <= 88 on a grid of fewer than 128 workgroups
+// whose waves each take more than 16 k-tiles, where the same GEMV in
+// launches of 64 tokens (each streaming the weights again) is faster
+// (measured, us, GEMV launches against prefill: N=14336, K=4096 M=65
+// 15.6/14.3, M=128 22.0/14.5; N=4096, K=4096 M=65 15.0/13.9; N=28672,
+// K=8192 M=65 41.0/39.2; N=4096, K=14336 M=65 30.0/36.5, M=80 33.4/36.5,
+// M=96 40.0/36.4);
+// M > 128: prefill.
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   const int ovr = g_ovr_path.load();
   if (M > kChunkMaxM || (M > kLutMaxM && ovr == 1)) return plan_prefill(M, N, K);
   if (M > kGemvMaxM) {
-    const long long prefill_tiles = (long long)((M + 63) / 64) * ((N + 255) / 256);
-    if (ovr < 0 && M > kChunkPrefillM && prefill_tiles >= kPrefillMinTiles) return plan_prefill(M, N, K);
+    const GemmPlan pf = plan_prefill(M, N, K);
+    const int kt_per_wave = (k_tiles(K) + pf.ch - 1) / pf.ch;
+    if (ovr < 0 && (M > kChunkPrefillM || pf.grid >= kPrefillMinGrid || kt_per_wave <= kPrefillMaxKtPerWave))
+      return pf;
     GemmPlan c = plan_mfma_gemv(kGemvMaxM, N, K);
     c.chunk = kGemvMaxM;
     return c;

@@ -17,7 +17,7 @@ struct GemmPlan {
   int kt_per_split;  // format k-tiles per K-split (GEMV)
   int rw;            // LUT GEMV: row tiles per workgroup; matrix-core GEMV: waves per
                      // row tile; prefill GEMM: tile height in units of 64 activation rows
-  int ch;            // k-tiles per LDS table stage (GEMV)
+  int ch;            // LUT GEMV: k-tiles per LDS table stage; prefill GEMM: k-phases (2 or 4)
   int groups;        // output row groups (GEMV)
   int lds_bytes;     // dynamic LDS per workgroup
   size_t ws_bytes;   // workspace bytes required
@@ -26,9 +26,10 @@ struct GemmPlan {
 
 constexpr int kLutMaxM = 16;          // M <= 16 takes a GEMV path
 constexpr int kGemvMaxM = 64;         // 16 < M <= 64: the matrix-core GEMV, unless path 1 is forced
-constexpr int kChunkMaxM = 128;       // 64 < M <= 128: the GEMV in launches of 64 tokens,
-constexpr int kChunkPrefillM = 96;    //   except above 96 tokens where the prefill GEMM's
-constexpr int kPrefillMinTiles = 96;  //   64-row tiles number at least 96 (wide N)
+constexpr int kChunkMaxM = 128;       // 64 < M <= 128: the prefill GEMM, unless at most 88
+constexpr int kChunkPrefillM = 88;    //   tokens, a grid under 128 workgroups and more than
+constexpr int kPrefillMinGrid = 128;  //   16 k-tiles per wave: then the GEMV in launches of
+constexpr int kPrefillMaxKtPerWave = 16;  // 64 tokens
 constexpr int kGemvWaves = 4;         // waves per GEMV workgroup
 constexpr int kDefaultSmallMPath = 2;  // M <= 16: 0 = lookup tables, 2 = matrix-core GEMV
 constexpr int kFuseMaxM = 4;           // fused quantization: at most 4 tokens,
@@ -100,8 +101,8 @@ bool lut_gemv_fusable(const GemmPlan& plan, int M, int K);
 // The same GEMV on the 2-bit baseline format (packed = kTile2Bytes tiles).
 hipError_t launch_mfma_gemv2(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 // The prefill GEMM's grid and LDS for tiles of bm (64 or 128) activation rows.
-int mfma_gemm_grid(int M, int N, int bm);
-int mfma_gemm_lds_bytes(int bm);
+int mfma_gemm_grid(int M, int N, int bm, int kp);
+int mfma_gemm_lds_bytes(int bm, int kp);
 int mfma_gemm_threads();
 hipError_t launch_mfma_gemm(const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 // The product (x int8) on the plan's path, in launches of plan.chunk tokens

@@ -264,8 +264,11 @@ sherry_status sherry_linear_plan(int64_t M, int64_t N, int64_t K, int* path,
  *          16 (at most 8 when M > 16);
  *          path 1 (forced): 1 or 2 = tiles of 64 or 128 tokens;
  *          0 (or a value the path does not take) = built-in choice.
- *   ch     path 0 only: k-tiles (128 inputs) per LDS table stage: 1, 2, 4
- *          or 8, capped so one stage stays within 32 KB; 0 = built-in.
+ *   ch     path 0: k-tiles (128 inputs) per LDS table stage: 1, 2, 4
+ *          or 8, capped so one stage stays within 32 KB;
+ *          path 1 (forced) with 64-token tiles: 2 or 4 k-phases (4: tiles
+ *          128 weight rows wide, each workgroup's K split four ways);
+ *          0 = built-in.
  *   splits K-splits per output row group; 0 = built-in choice.
  * Results do not depend on the plan.  sherry_workspace_bytes reflects the
  * override, so query it after setting one.  Not thread-safe with respect to

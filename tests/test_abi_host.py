@@ -83,9 +83,12 @@ def test_plan_dispatch_rule():
     for M in (17, 31, 64):
         p = bw.plan(M, 4096, 4096)
         assert p["path"] == "decode_mfma_gemv" and p["block"] <= 512   # at most 8 waves
-    for M in (65, 100, 128):   # launches of 64 tokens on the GEMV
-        assert bw.plan(M, 4096, 4096)["path"] == "decode_mfma_gemv"
-        assert bw.workspace_bytes(M, 4096, 4096) in (0, 64 * 4096 * 8)
+    for M in (65, 100, 128):   # the prefill's 64-token tiles with 4 k-phases
+        assert bw.plan(M, 4096, 4096)["path"] == "decode_mfma"
+        assert bw.workspace_bytes(M, 4096, 4096) == 0
+    for M in (65, 88):         # small grid, long K: launches of 64 tokens on the GEMV
+        assert bw.plan(M, 4096, 14336)["path"] == "decode_mfma_gemv"
+        assert bw.workspace_bytes(M, 4096, 14336) in (0, 64 * 4096 * 8)
     for M in (129, 130, 512):
         assert bw.plan(M, 4096, 4096)["path"] == "decode_mfma"
     p = bw.plan(1, 4096, 4096)
@@ -98,36 +101,31 @@ def test_plan_dispatch_rule():
 
 def test_prefill_tile_height_rule():
     """The prefill GEMM takes tiles of 64 tokens when that grid fits the GPU
-    in one round (<= 256 tiles of 256 weight rows), else 128; above 96
-    tokens it replaces the 64-token GEMV launches when its 64-token tiles
-    number >= 96."""
-    lds64, lds128 = 78080, 107008      # the two kernels' LDS per workgroup
-    def tiles(M, N, bm):
-        return -(-M // bm) * -(-N // 256)
+    in one round (<= 256 tiles of 256 weight rows), else 128; with 64-token
+    tiles it takes 4 k-phases (tiles of 128 weight rows) when that doubled
+    grid still fits, else 2.  Between 65 and 128 tokens it is the default,
+    except at M <= 88 on a grid under 128 workgroups with more than 16
+    k-tiles per wave, where the 64-token GEMV launches stay."""
+    lds64, lds64kp4, lds128 = 78080, 106752, 107008   # the three kernels' LDS per workgroup
+    def tiles(M, N, bm, bn):
+        return -(-M // bm) * -(-N // bn)
     for M, N in [(129, 14336), (200, 14336), (256, 14336), (257, 14336), (512, 14336),
-                 (300, 4096), (1000, 4096), (1100, 4096), (129, 65536)]:
+                 (128, 4096), (136, 4096), (300, 4096), (1000, 4096), (1100, 4096), (129, 65536)]:
         p = bw.plan(M, N, 4096)
         assert p["path"] == "decode_mfma"
-        want64 = tiles(M, N, 64) <= 256
-        assert p["lds_bytes"] == (lds64 if want64 else lds128), (M, N)
-        nt = -(-N // 256)
+        want64 = tiles(M, N, 64, 256) <= 256
+        kp4 = want64 and tiles(M, N, 64, 128) <= 256
+        assert p["lds_bytes"] == (lds64kp4 if kp4 else lds64 if want64 else lds128), (M, N)
+        nt = -(-N // (128 if kp4 else 256))
         assert p["grid"] == 8 * -(-nt // 8) * -(-M // (64 if want64 else 128)), (M, N)
-    # 96 < M <= 128: the prefill for wide N (>= 96 tiles of 64 tokens), else the GEMV launches
-    for M, N, want in [(96, 14336, "decode_mfma_gemv"), (97, 14336, "decode_mfma"),
-                       (128, 14336, "decode_mfma"), (128, 12288, "decode_mfma"),
-                       (128, 11008, "decode_mfma_gemv"), (100, 4096, "decode_mfma_gemv"),
-                       (65, 65536, "decode_mfma_gemv")]:
-        assert bw.plan(M, N, 4096)["path"] == want, (M, N)
-    try:   # forcing the GEMV keeps it there; forcing the prefill picks the height by rw
-        bw.plan_override("decode_mfma_gemv")
-        assert bw.plan(128, 14336, 4096)["path"] == "decode_mfma_gemv"
-        bw.plan_override("decode_mfma", 2)
-        assert bw.plan(100, 4096, 4096)["lds_bytes"] == lds128
-        bw.plan_override("decode_mfma", 1)
-        assert bw.plan(512, 14336, 4096)["lds_bytes"] == lds64
-        assert bw.plan(512, 14336, 4096)["grid"] == 8 * 7 * 8
-    finally:
-        bw.plan_override()
+    # 64 < M <= 128: the prefill, but the GEMV launches on a small grid with long K at M <= 88
+    for M, N, K, want in [(65, 14336, 4096, "decode_mfma"), (96, 14336, 4096, "decode_mfma"),
+                          (128, 14336, 4096, "decode_mfma"), (65, 4096, 4096, "decode_mfma"),
+                          (100, 4096, 4096, "decode_mfma"), (65, 28672, 8192, "decode_mfma"),
+                          (80, 4096, 14336, "decode_mfma_gemv"), (88, 4096, 14336, "decode_mfma_gemv"),
+                          (89, 4096, 14336, "decode_mfma"), (65, 1024, 8192, "decode_mfma"),
+                          (65, 1024, 8448, "decode_mfma_gemv")]:
+        assert bw.plan(M, N, K)["path"] == want, (M, N, K)
 
 
 def test_plan_override_changes_plan_and_workspace():
@@ -342,16 +340,18 @@ def test_plan_invariants_over_random_shapes():
         assert 0 < p["lds_bytes"] <= 160 * 1024, (M, N, K, p)
         if M <= 16:
             assert p["path"] in ("lut_gemv", "decode_mfma_gemv"), (M, N, K, p)
-        elif M <= 96:
+        elif M <= 64:
             assert p["path"] == "decode_mfma_gemv", (M, N, K, p)
-        elif M > 128:
+        elif M > 88:
             assert p["path"] == "decode_mfma", (M, N, K, p)
         ws = bw.workspace_bytes(M, N, K)
         if p["path"] == "decode_mfma":
             assert p["splits"] == 1 and ws == 0
-            bm = 64 if p["lds_bytes"] == 78080 else 128
-            assert p["lds_bytes"] in (78080, 107008)
-            assert p["grid"] == 8 * -(-(-(-N // 256)) // 8) * -(-M // bm), (M, N, K, p)
+            # 64-token tiles (2 or 4 k-phases: 256- or 128-row tiles) or 128-token tiles
+            bm, bn = {78080: (64, 256), 106752: (64, 128), 107008: (128, 256)}[p["lds_bytes"]]
+            assert p["grid"] == 8 * -(-(-(-N // bn)) // 8) * -(-M // bm), (M, N, K, p)
+            # 4 k-phases only when the real tiles (the grid less its XCD padding) fit one round
+            assert -(-M // bm) * -(-N // bn) <= 256 or bn == 256, (M, N, K, p)
             continue
         s = p["splits"]
         assert 1 <= s <= KT and -(-KT // -(-KT // s)) == s, (M, N, K, p)   # no empty split

@@ -337,20 +337,22 @@ def test_linear_fused_unsplit_long_waves(orc, rw, K, M):
     assert_y_close(gl.cpu().numpy(), y)
 
 
-@pytest.mark.parametrize("bm", [1, 2])                 # tiles of 64 or 128 tokens
+@pytest.mark.parametrize("bm,kp", [(1, 2), (1, 4), (2, 0)])  # 64-token tiles, 2 or 4 k-phases; 128
 @pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64, 65, 100, 128, 129, 200, 300])
-def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M, bm):
+def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M, bm, kp):
     """The prefill kernel forced onto small and mid M with either tile height
-    (rows past M clamped, a ragged last token tile)."""
+    and, for 64-token tiles, 2 or 4 k-phases (rows past M clamped, a ragged
+    last token tile, N = 320 ragged against 128- and 256-row tiles, 9
+    k-tiles: a short last step with 2 and with 4 phases)."""
     N, K = 320, 1152
     T, alpha, packed, galpha = packed_cases[(N, K)]
     q = synth.int8_uniform(M, K, seed=2900 + M)
     acc = orc.gemm_i32(q.numpy(), T)
     try:
-        bw.plan_override("decode_mfma", bm)
+        bw.plan_override("decode_mfma", bm, kp)
         p = bw.plan(M, N, K)
         assert p["path"] == "decode_mfma"
-        assert p["grid"] == 8 * 1 * -(-M // (64 * bm))   # 2 n tiles -> one per XCD slot
+        assert p["grid"] == 8 * 1 * -(-M // (64 * bm))   # 2 or 3 n tiles -> one per XCD slot
         gacc = bw.gemm_i32(q.cuda(), packed, N, K)
         torch.cuda.synchronize()
     finally:
@@ -446,13 +448,13 @@ def workload_5_ref(orc):
     return w, acc, y, packed, galpha, gq, gs
 
 
-@pytest.mark.parametrize("bm", [0, 1, 2])    # built-in tiles, or 64 / 128 tokens forced
-def test_workload_5_prefill_full(workload_5_ref, bm):
+@pytest.mark.parametrize("bm,kp", [(0, 0), (1, 2), (1, 4), (2, 0)])  # built-in, or forced tiles / k-phases
+def test_workload_5_prefill_full(workload_5_ref, bm, kp):
     """Every one of the 7.3 M outputs of workload 5: int32 bit-exact, fp32
     within 1e-5 (bit-identical in practice)."""
     w, acc, y, packed, galpha, gq, gs = workload_5_ref
     try:
-        bw.plan_override("decode_mfma" if bm else None, bm)
+        bw.plan_override("decode_mfma" if bm else None, bm, kp)
         _say(f"workload 5 full: {bw.plan(w.M, w.N, w.K)}")
         gacc = bw.gemm_i32(gq, packed, w.N, w.K).cpu().numpy()
         gy = bw.gemm(gq, gs, packed, galpha, w.N, w.K).cpu().numpy()
@@ -487,19 +489,19 @@ def test_random_shapes_every_path(orc, M, N, K):
     packed, galpha = gpu_pack(W)
     assert np.array_equal(packed.cpu().numpy(), orc.pack(T)), "packed codes"
     gq, gs = bw.quantize_act(x.cuda())
-    paths = [(None, 0), ("decode_mfma", 1), ("decode_mfma", 2)]
+    paths = [(None, 0, 0), ("decode_mfma", 1, 2), ("decode_mfma", 1, 4), ("decode_mfma", 2, 0)]
     if M <= 16:
-        paths += [("lut_gemv", 0), ("decode_mfma_gemv", 0)]
+        paths += [("lut_gemv", 0, 0), ("decode_mfma_gemv", 0, 0)]
     elif M <= 128:
-        paths += [("decode_mfma_gemv", 0)]
-    for path, rw in paths:
+        paths += [("decode_mfma_gemv", 0, 0)]
+    for path, rw, ch in paths:
         try:
-            bw.plan_override(path, rw)
-            _say(f"random M={M} N={N} K={K} path {path}/{rw}: {bw.plan(M, N, K)}")
+            bw.plan_override(path, rw, ch)
+            _say(f"random M={M} N={N} K={K} path {path}/{rw}/{ch}: {bw.plan(M, N, K)}")
             gacc = bw.gemm_i32(gq, packed, N, K).cpu().numpy()
         finally:
             bw.plan_override()
-        assert np.array_equal(gacc, acc), f"acc ({path}, {rw})"
+        assert np.array_equal(gacc, acc), f"acc ({path}, {rw}, {ch})"
     gy = bw.linear(x.cuda(), packed, galpha, N, K)
     torch.cuda.synchronize()
     assert_y_close(gy.cpu().numpy(), y)
@@ -515,13 +517,14 @@ def test_random_shapes_every_path(orc, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 8192, 28672), (8, 8192, 28672), (16, 8192, 28672),
                                    (9, 4096, 4096), (16, 4096, 11008), (64, 4096, 4096),
-                                   (128, 4096, 4096)])
+                                   (88, 4096, 14336)])
 def test_gemm_gemv_plan_rule_shapes(orc, M, N, K):
     """The GEMV plans the built-in rule picks at these shapes: K split at
     wide N and long K for one token block (a wave keeps at most 8 or 16
     k-tiles), and 8 waves per row tile with few splits above 8 tokens at
-    narrow N (one split at K=4096, 64-token launches at M=128): y and the
-    int32 sums against the oracle."""
+    narrow N (one split at K=4096; launches of 64 + 24 tokens at M=88,
+    K=14336, where the prefill's grid is small and its waves' K long): y and
+    the int32 sums against the oracle."""
     W = synth.weights(N, K, 0.02, False, seed=9300 + N + K)
     x = synth.activations(M, K, seed=9400 + M + K)
     T, alpha = orc.quantize(W.numpy())
