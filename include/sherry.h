@@ -134,13 +134,16 @@ sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
  *            block and token pair);
  *   16 < M <= 64: the matrix-core GEMV with the tokens in two or four
  *            blocks of 16;
- *   64 < M <= 128: that GEMV in launches of 64 tokens on the same stream
- *            (sherry_workspace_bytes covers one launch); above 96 tokens
- *            the prefill GEMM instead when its 64-token tiles number at
- *            least 96 (wide N);
+ *   64 < M <= 128: the prefill GEMM below, except at M <= 88 when its
+ *            grid is under 128 workgroups and each wave would take more
+ *            than 16 k-tiles: then that GEMV in launches of 64 tokens on
+ *            the same stream (sherry_workspace_bytes covers one launch);
  *   M > 128: the prefill GEMM on the int8 matrix cores: workgroup tiles of
  *            64 tokens x 256 weight rows when that grid fits the GPU in one
- *            round (at most 256 tiles), else 128 tokens x 256 rows. */
+ *            round (at most 256 tiles), else 128 tokens x 256 rows; 64-token
+ *            tiles split each workgroup's K over 4 wave phases instead of 2
+ *            (tiles 128 weight rows wide) when twice the tiles still fit one
+ *            round. */
 sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           const float* alpha, float* y, int64_t M, int64_t N,
                           int64_t K, void* workspace, size_t workspace_bytes,
