@@ -31,8 +31,9 @@
 //    weight row 16t + l%16 and, for lane group g = l/16, codes 8g..8g+7 of
 //    the k-tile (inputs 32g..32g+31: the first half in MFMA sub-step 0, the
 //    second in sub-step 1): dword t and byte t of the slot's last dword.  The
-//    A operands use the same input order, which a dot product does not see.  A 1024-entry LDS table maps a 10-bit code
-//    pair to its 8 int8 weights, so 4 codes cost two 8-byte lookups;
+//    A operands use the same input order, which a dot product does not see.
+//    A 1024-entry LDS table maps a 10-bit code pair to its 8 int8 weights,
+//    so 4 codes cost two 8-byte lookups;
 //  * codes come through a buffer descriptor into two register stages used
 //    in turn; a k-step's codes are decoded (table lookups) between the
 //    MFMAs of the step before it, so the LDS lookups overlap matrix-core
@@ -442,11 +443,13 @@ hipError_t launch_tiles(const GemmPlan& p, const GemmArgs& a, hipStream_t stream
 
 }  // namespace
 
+// Static LDS per workgroup: activation buffers (or epilogue tiles), the pair
+// table, the tile's s_x and, with 128-row tiles, the two phase counters.
 int mfma_gemm_lds_bytes(int bm, int kp) {
   const int main_bytes = bm == 128 ? Tiling<128, 2>::kLdsBytes
                          : kp == 4 ? Tiling<64, 4>::kLdsBytes
                                    : Tiling<64, 2>::kLdsBytes;
-  return main_bytes + 1024 * 8 + bm * 4;
+  return main_bytes + 1024 * 8 + bm * 4 + (bm == 128 ? 8 : 0);
 }
 
 int mfma_gemm_threads() { return kThreads; }

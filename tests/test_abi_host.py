@@ -106,7 +106,7 @@ def test_prefill_tile_height_rule():
     grid still fits, else 2.  Between 65 and 128 tokens it is the default,
     except at M <= 88 on a grid under 128 workgroups with more than 16
     k-tiles per wave, where the 64-token GEMV launches stay."""
-    lds64, lds64kp4, lds128 = 78080, 106752, 107008   # the three kernels' LDS per workgroup
+    lds64, lds64kp4, lds128 = 78080, 106752, 107016   # the three kernels' LDS per workgroup
     def tiles(M, N, bm, bn):
         return -(-M // bm) * -(-N // bn)
     for M, N in [(129, 14336), (200, 14336), (256, 14336), (257, 14336), (512, 14336),
@@ -348,7 +348,7 @@ def test_plan_invariants_over_random_shapes():
         if p["path"] == "decode_mfma":
             assert p["splits"] == 1 and ws == 0
             # 64-token tiles (2 or 4 k-phases: 256- or 128-row tiles) or 128-token tiles
-            bm, bn = {78080: (64, 256), 106752: (64, 128), 107008: (128, 256)}[p["lds_bytes"]]
+            bm, bn = {78080: (64, 256), 106752: (64, 128), 107016: (128, 256)}[p["lds_bytes"]]
             assert p["grid"] == 8 * -(-(-(-N // bn)) // 8) * -(-M // bm), (M, N, K, p)
             # 4 k-phases only when the real tiles (the grid less its XCD padding) fit one round
             assert -(-M // bm) * -(-N // bn) <= 256 or bn == 256, (M, N, K, p)
