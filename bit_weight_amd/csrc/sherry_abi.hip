@@ -223,18 +223,26 @@ GemmPlan plan_gemm(int M, int N, int K) {
   int ch_max = 1;                       // one stage of tables stays <= 32 KB
   while (ch_max < 8 && (ch_max * 2) * MP <= 8) ch_max *= 2;
 
-  // Built-in plan from a sweep of row tiles per workgroup x table stage x
-  // K-splits on MI355X (M=1 at K=4096 and 11008, M=4 and 16 at K=N=4096,
-  // M=8 at K=8192, N=28672): up to 4 tokens, one row tile per workgroup
-  // (its 4 waves share it); above, 4 row tiles of one wave each.  K-splits
-  // of 2 k-tiles for 1-2 tokens and above 8, else 4, at most 16 splits:
-  // more workgroups keep more lookups in flight, and the 64-bit cell
-  // atomics of the splits cost less than idle CUs (M=16: 24.3 -> 17.4 us,
-  // M=4: 8.0 -> 6.1, M=8 at N=28672: 42.7 -> 33.8 against 512 workgroups).
-  int rw = g_ovr_rw.load() > 0 ? g_ovr_rw.load() : (M > 4 ? 4 : 1);
+  // Built-in plan from sweeps of row tiles per workgroup x table stage x
+  // K-splits on MI355X (M = 1..16 at N = 4096..28672, K = 4096..11008):
+  // row tiles per workgroup (its 4 waves are rw row tiles x 4/rw waves
+  // sharing one): up to 4 tokens 1, or 2 from 128 row tiles; up to 8
+  // tokens 2; above 8 tokens 4; and 4 from 448 row tiles.  K-splits of 2
+  // k-tiles for 1-2 tokens, and above 8 tokens below 128 row tiles, of 8
+  // above 8 tokens from 448 row tiles, else 4, at most 16 splits: more
+  // workgroups keep more lookups in flight, and the 64-bit cell atomics of
+  // the splits cost less than idle CUs.  One k-tile per table stage with 4
+  // row tiles, else the largest stage that fits.  Measured against the
+  // earlier rule (1 or 4 row tiles, stages as large as fit, 2-k-tile splits
+  // above 8 tokens), us: M=8 at N=28672, K=8192 39.3 -> 34.0; M=6 there
+  // 40.1 -> 26.7; M=16 there 70.0 -> 60.0; M=1 there 17.3 -> 14.3; M=8 at
+  // N=K=4096 12.9 -> 9.9; M=12 at N=14336, K=4096 27.0 -> 22.0; M=1 at
+  // N=14336, K=4096 7.3 -> 6.2; M=4 at N=11008 10.8 -> 9.4.
+  const int rw_def = RT >= 448 || M > 8 ? 4 : M > 4 ? 2 : RT >= 128 ? 2 : 1;
+  int rw = g_ovr_rw.load() > 0 ? g_ovr_rw.load() : rw_def;
   if (rw != 1 && rw != 2 && rw != 4) rw = 4;
   const int G = (RT + rw - 1) / rw;
-  const int kt_per_split_def = (M <= 2 || M > 8) ? 2 : 4;
+  const int kt_per_split_def = M <= 2 ? 2 : M <= 8 ? 4 : RT < 128 ? 2 : RT < 448 ? 4 : 8;
   int splits = g_ovr_splits.load() > 0 ? g_ovr_splits.load() : KT / kt_per_split_def;
   if (splits > 16 && g_ovr_splits.load() <= 0) splits = 16;
   if (splits > KT) splits = KT;
@@ -242,7 +250,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
   const int kt_per_split = (KT + splits - 1) / splits;
   splits = (KT + kt_per_split - 1) / kt_per_split;
   int ch = 1;
-  const int ch_cap = g_ovr_ch.load() > 0 ? g_ovr_ch.load() : ch_max;
+  const int ch_cap = g_ovr_ch.load() > 0 ? g_ovr_ch.load() : (rw == 4 ? 1 : ch_max);
   while (ch * 2 <= ch_cap && ch * 2 <= ch_max && ch * 2 <= kt_per_split) ch *= 2;
 
   const int kw = kGemvWaves / rw;
