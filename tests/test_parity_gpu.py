@@ -476,7 +476,7 @@ def _random_shapes(n, seed):
     return out
 
 
-@pytest.mark.parametrize("M,N,K", _random_shapes(30, 9090))
+@pytest.mark.parametrize("M,N,K", _random_shapes(60, 9090))
 def test_random_shapes_every_path(orc, M, N, K):
     """Seeded random shapes over the whole shape rule: the int32 product on
     every path that takes the shape, sherry_linear and (M <= 16) the 2-bit
