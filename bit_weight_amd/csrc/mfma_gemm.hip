@@ -11,9 +11,9 @@
 // SIMD: wave (kh, w) takes the k-tiles of phase kh (2j + kh) of row tile w,
 // i.e. 64 weight rows = 4 MFMA column blocks, against all 128 activation
 // rows = 8 MFMA row blocks (8 x 4 accumulators); the two phases' sums are
-// added in the epilogue.  With 64-row tiles on a small grid the 8 waves
-// split instead into 2 row tiles x KP = 4 k-phases (BN = 128, k-tiles
-// 4j + kh): twice the workgroups, each a quarter of K per wave.
+// added in the epilogue.  On a small grid the 8 waves split instead into 2
+// row tiles x KP = 4 k-phases (BN = 128, k-tiles 4j + kh): twice the
+// workgroups, each a quarter of K per wave; BM = 64 halves the tile again.
 // A decoded weight operand therefore feeds 8 MFMAs and an activation
 // fragment 4, which keeps the LDS work per k-tile (pair-table lookups plus
 // activation fragments) well below the matrix-core time.
@@ -24,7 +24,9 @@
 //    XOR-swizzled (see a_off) so the MFMA A reads (16 rows, one chunk) hit 16
 //    different bank groups.  Three buffers per phase: the copy for k-step
 //    j+2 starts right after the barrier of step j, once every wave is done
-//    with the buffer it overwrites, and has two steps to land;
+//    with the buffer it overwrites, and has two steps to land (two buffers
+//    and one step with BM = 128 and 4 phases, whose 12 x 16 KB would not
+//    fit LDS);
 //  * weights: each wave decodes exactly the B operands it consumes.  It loads
 //    its row tile's 1280-byte k-tile coalesced (lane l = slot l, 16 + 4
 //    bytes), which by the format's design already holds, for column block t,
@@ -55,14 +57,17 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kNT = kTileRows / 16;             // 4 column blocks per wave (one row tile)
 constexpr int kBK = kTileK;                     // 128
-constexpr int kABufs = 3;                       // activation buffers per k-phase
 constexpr int kThreads = 512;                   // 8 waves: row tiles x k-phases
 
 // The sizes that follow from the tile height BM (128 or 64 activation rows)
-// and the number of k-phases KP (2, or 4 with 64-row tiles).
+// and the number of k-phases KP (2 or 4).
 template <int BM, int KP>
 struct Tiling {
-  static_assert(KP == 2 || (KP == 4 && BM == 64), "k-phases: 2, or 4 with 64-row tiles");
+  static_assert(KP == 2 || KP == 4, "k-phases: 2 or 4");
+  // activation buffers per k-phase: three (the copy for step j+2 issued in
+  // step j), or two with 128-row tiles and 4 phases, whose 4 x 3 x 16 KB
+  // would not fit LDS (the copy for step j+1 issued in step j)
+  static constexpr int kABufs = BM == 128 && KP == 4 ? 2 : 3;
   static constexpr int kRT = kThreads / 64 / KP;       // row tiles per workgroup (4 or 2)
   static constexpr int kBN = kRT * kTileRows;          // workgroup tile width (256 or 128 weight rows)
   static constexpr int kOutLd = kBN + 16;              // words per row of the epilogue tiles (the 4
@@ -75,9 +80,10 @@ struct Tiling {
   static constexpr int kLdsMain = KP * kABufs * kAStage;  // activation buffers x phases
   static constexpr int kLdsBytes = kLdsMain > kLdsOut ? kLdsMain : kLdsOut;
   // vector-memory ops a wave issues between a k-step's activation copy and
-  // that step's barrier: the codes three steps ahead of it (2), the next
-  // step's copy, and the codes four steps ahead (2)
-  static constexpr int kNewerLoads = 2 + kACopies + 2;
+  // that step's barrier: with three buffers the codes three steps ahead of
+  // it (2), the next step's copy, and the codes four steps ahead (2); with
+  // two, the codes two steps ahead of it (2)
+  static constexpr int kNewerLoads = kABufs == 3 ? 2 + kACopies + 2 : 2;
 };
 
 // Activation tile in LDS, row-major with 128-byte rows: the 16-byte chunk c
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   using T = Tiling<BM, KP>;
   constexpr int kBM = BM, kMT = T::kMT, kAStage = T::kAStage, kACopies = T::kACopies;
   constexpr int kLdsBytes = T::kLdsBytes, kNewerLoads = T::kNewerLoads;
-  constexpr int kRT = T::kRT, kBN = T::kBN, kOutLd = T::kOutLd;
+  constexpr int kRT = T::kRT, kBN = T::kBN, kOutLd = T::kOutLd, kABufs = T::kABufs;
   // the activation buffers [buffer][phase]; after the main loop the
   // epilogue tile reuses them
   // (32-bit words: every view below is a character type or 32-bit lanes)
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   __shared__ __attribute__((aligned(1024))) uint2 dec2[1024];
   __shared__ float sxs[kBM];   // s_x of this tile's rows (epilogue)
   // arrivals at the step barrier of each k-tile parity (128-row tiles)
-  __shared__ unsigned parity_arrivals[2];
+  __shared__ unsigned parity_arrivals[KP];
 
   const int KT = k_tiles(K), RT = row_tiles(N);
   // tile id -> (m tile, n tile): consecutive ids of one XCD share n tiles
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   const int wave = wv % kRT, kh = wv / kRT;        // row tile, k-phase
   const int l16 = lane & 15, g = lane >> 4;
 
-  if (tid < 2) parity_arrivals[tid] = 0u;   // published by the prologue's barrier
+  if (tid < KP) parity_arrivals[tid] = 0u;   // published by the prologue's barrier
   // decode table: code pair (c0 | c1 << 5) -> the 8 int8 weights of both
   for (int i = tid; i < 1024; i += kThreads)
     dec2[i] = make_uint2(code_word(i & 31), code_word(i >> 5));
@@ -292,14 +298,14 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
       asm volatile("" : "+v"(f0[t]), "+v"(f1[t]));
     }
   };
-  // Step j (activation buffer b = j % 3): its B operands bc0 / bc1 were
+  // Step j (activation buffer b = j % kABufs): its B operands bc0 / bc1 were
   // decoded during step j-1; the register stage (wn, hn) holds the codes of
   // step j+1, decoded during this step's MFMAs into bn0 / bn1 and then
   // refilled with the codes of step j+3.
-  // The step barrier.  With 128-row tiles it joins only the 4 waves of this
-  // wave's k-tile parity, which share that parity's activation buffers and
-  // nothing else until the epilogue: an LDS arrival count per parity, so the
-  // two parities' waves (two to a SIMD) need not leave each step together
+  // The step barrier.  With 128-row tiles it joins only the kRT waves of
+  // this wave's k-phase, which share that phase's activation buffers and
+  // nothing else until the epilogue: an LDS arrival count per phase, so the
+  // phases' waves (two to a SIMD) need not leave each step together
   // (measured at N=14336, K=4096: M=512 31.7 -> 30.6 us, M=1024 66.6 ->
   // 60.6; with 64-row tiles it was 2 % slower, so those keep s_barrier).
   // The arrival and the polls are LDS instructions in asm: as built-ins the
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   auto parity_barrier = [&](int j) {
     const uint32_t pa = (uint32_t)(size_t)((__attribute__((address_space(3))) unsigned*)&parity_arrivals[kh]);
     if (lane == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(pa), "v"(1u) : "memory");
-    const unsigned target = 4u * (unsigned)(j + 1);
+    const unsigned target = (unsigned)kRT * (unsigned)(j + 1);
     for (int spin = 0; spin < (1 << 22); ++spin) {
       unsigned c;
       asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(c) : "v"(pa) : "memory");
@@ -329,7 +335,10 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
       __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     __builtin_amdgcn_sched_barrier(0);
-    copy_a(min(j + 2, KJ - 1), b == 0 ? 2 : b - 1);
+    if constexpr (kABufs == 3)
+      copy_a(min(j + 2, KJ - 1), b == 0 ? 2 : b - 1);
+    else
+      copy_a(min(j + 1, KJ - 1), b ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     uint32_t f0[kNT], f1[kNT];
     split(wn, hn, f0, f1);
@@ -343,8 +352,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
 
   // Two register stages of codes and two sets of B operands, ping-pong.
   // Issue order (the barrier's vmcnt counts on it): codes 0, copy 0,
-  // codes 1, copy 1, codes 2, then per step j: barrier, copy j+2,
-  // codes j+3.
+  // codes 1, copy 1 (three buffers only), codes 2, then per step j:
+  // barrier, copy j+2 (j+1 with two buffers), codes j+3.
   v4u w0, w1;
   uint32_t h0, h1;
   v4i bA0[kNT], bA1[kNT], bB0[kNT], bB1[kNT];
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   __builtin_amdgcn_sched_barrier(0);
   load_codes(min(1, KJ - 1), w1, h1);
   __builtin_amdgcn_sched_barrier(0);
-  copy_a(min(1, KJ - 1), 1);
+  if constexpr (kABufs == 3) copy_a(min(1, KJ - 1), 1);
   __builtin_amdgcn_sched_barrier(0);
   // decode table written (LDS only: the copies stay in flight)
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
@@ -376,9 +385,9 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   int j = 0, b = 0;
   for (; j + 2 <= KJ; j += 2) {
     step(j, b, w1, h1, bA0, bA1, bB0, bB1);
-    b = b == 2 ? 0 : b + 1;
+    b = b + 1 == kABufs ? 0 : b + 1;
     step(j + 1, b, w0, h0, bB0, bB1, bA0, bA1);
-    b = b == 2 ? 0 : b + 1;
+    b = b + 1 == kABufs ? 0 : b + 1;
   }
   if (j < KJ) step(j, b, w1, h1, bA0, bA1, bB0, bB1);
   // the clamped copies past the end may still be landing in LDS, which the
@@ -444,12 +453,12 @@ hipError_t launch_tiles(const GemmPlan& p, const GemmArgs& a, hipStream_t stream
 }  // namespace
 
 // Static LDS per workgroup: activation buffers (or epilogue tiles), the pair
-// table, the tile's s_x and, with 128-row tiles, the two phase counters.
+// table, the tile's s_x and, with 128-row tiles, the phase counters.
 int mfma_gemm_lds_bytes(int bm, int kp) {
-  const int main_bytes = bm == 128 ? Tiling<128, 2>::kLdsBytes
+  const int main_bytes = bm == 128 ? (kp == 4 ? Tiling<128, 4>::kLdsBytes : Tiling<128, 2>::kLdsBytes)
                          : kp == 4 ? Tiling<64, 4>::kLdsBytes
                                    : Tiling<64, 2>::kLdsBytes;
-  return main_bytes + 1024 * 8 + bm * 4 + (bm == 128 ? 8 : 0);
+  return main_bytes + 1024 * 8 + bm * 4 + (bm == 128 ? 4 * kp : 0);
 }
 
 int mfma_gemm_threads() { return kThreads; }
@@ -462,10 +471,11 @@ int mfma_gemm_grid(int M, int N, int bm, int kp) {
 }
 
 // plan.rw carries the tile height in units of 64 activation rows (1 or 2),
-// plan.ch the k-phases (2, or 4 with 64-row tiles).
+// plan.ch the k-phases (2 or 4).
 hipError_t launch_mfma_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   if (p.rw == 1 && p.ch == 4) return launch_tiles<64, 4>(p, a, stream);
   if (p.rw == 1 && p.ch == 2) return launch_tiles<64, 2>(p, a, stream);
+  if (p.rw == 2 && p.ch == 4) return launch_tiles<128, 4>(p, a, stream);
   if (p.rw == 2 && p.ch == 2) return launch_tiles<128, 2>(p, a, stream);
   return hipErrorInvalidValue;
 }

@@ -157,26 +157,38 @@ hipError_t launch_product(const GemmPlan& plan, const GemmArgs& args, hipStream_
 }
 
 namespace {
-// Prefill GEMM: one workgroup per 128 x 256 output tile, no K-split.
-// Tiles of 64 activation rows when that grid fits the GPU in one round
-// (<= 256 workgroups), else 128: per workgroup the 128-row tile costs half
-// the decode per multiply-add, but below ~256 tokens it leaves CUs idle
-// (M=129..256 at N=14336: 112 tiles of 128 rows).  A forced prefill path
-// with rw = 1 or 2 in the override picks the height.
+// Prefill GEMM: one workgroup per output tile (64 or 128 tokens x 128 or
+// 256 weight rows), no K-split across workgroups.  A tile of 128 tokens
+// costs half the decode per multiply-add, a tile of 128 weight rows splits
+// each wave's K loop in four instead of two; the smaller tiles pay when the
+// larger leave CUs idle (M=129..256 at N=14336: 112 tiles of 128 x 256).
+// A forced prefill path with rw = 1 or 2 in the override picks the height,
+// with ch = 2 or 4 the k-phases.
 GemmPlan plan_prefill(int M, int N, int K) {
   GemmPlan p{};
-  const long long mt64 = (M + 63) / 64;
-  int bm = mt64 * ((N + 255) / 256) <= 256 ? 64 : 128;
+  // Tiles in order of preference, the first whose grid fits the GPU in one
+  // round (at most 256 tiles): 64 tokens x 128 weight rows with each
+  // workgroup's K split over 4 wave phases; 128 x 128 with 4 phases; 64 x
+  // 256 with 2 phases; else 128 x 256 with 2.  Splitting K four ways halves
+  // each wave's loop on twice the workgroups (measured at K=4096, M=128:
+  // N=14336 20.6 -> 14.5 us, N=4096 20.4 -> 14.2; at M=136, N=4096,
+  // K=14336 56.3 -> 36.3), and 128-token tiles halve the decode per
+  // multiply-add (M=129..256, N=14336, K=4096: 64 x 256 tiles 20.4 us,
+  // 128 x 128 tiles 18.6).
+  const long long mt64 = (M + 63) / 64, mt128 = (M + 127) / 128;
+  const long long nt128 = (N + 127) / 128, nt256 = (N + 255) / 256;
+  int bm = 128, kp = 2;
+  if (mt64 * nt128 <= 256) bm = 64, kp = 4;
+  else if (mt128 * nt128 <= 256) bm = 128, kp = 4;
+  else if (mt64 * nt256 <= 256) bm = 64, kp = 2;
   const int ovr_rw = g_ovr_rw.load();
   const bool forced = g_ovr_path.load() == 1;
-  if (forced && (ovr_rw == 1 || ovr_rw == 2)) bm = 64 * ovr_rw;
-  // 64-row tiles split each workgroup's K four ways when twice the
-  // workgroups still fit the GPU in one round (tiles 128 weight rows wide):
-  // measured at K=4096, M=128: N=14336 20.6 -> 14.5 us, N=4096 20.4 -> 14.2;
-  // at M=136, N=4096, K=14336 56.3 -> 36.3
-  int kp = bm == 64 && mt64 * ((N + 127) / 128) <= 256 ? 4 : 2;
+  if (forced && (ovr_rw == 1 || ovr_rw == 2)) {
+    bm = 64 * ovr_rw;
+    kp = (bm == 64 ? mt64 : mt128) * nt128 <= 256 ? 4 : 2;
+  }
   const int ovr_ch = g_ovr_ch.load();
-  if (forced && bm == 64 && (ovr_ch == 2 || ovr_ch == 4)) kp = ovr_ch;
+  if (forced && (ovr_ch == 2 || ovr_ch == 4)) kp = ovr_ch;
   p.path = 1;
   p.rw = bm / 64;
   p.ch = kp;

@@ -138,12 +138,11 @@ sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
  *            grid is under 128 workgroups and each wave would take more
  *            than 16 k-tiles: then that GEMV in launches of 64 tokens on
  *            the same stream (sherry_workspace_bytes covers one launch);
- *   M > 128: the prefill GEMM on the int8 matrix cores: workgroup tiles of
- *            64 tokens x 256 weight rows when that grid fits the GPU in one
- *            round (at most 256 tiles), else 128 tokens x 256 rows; 64-token
- *            tiles split each workgroup's K over 4 wave phases instead of 2
- *            (tiles 128 weight rows wide) when twice the tiles still fit one
- *            round. */
+ *   M > 128: the prefill GEMM on the int8 matrix cores, in the first
+ *            workgroup tile whose grid fits the GPU in one round (at most
+ *            256 tiles): 64 tokens x 128 weight rows, 128 x 128, 64 x 256,
+ *            else 128 x 256; tiles 128 rows wide split each workgroup's K
+ *            over 4 wave phases, 256 rows wide over 2. */
 sherry_status sherry_gemm(const int8_t* x, const float* s_x, const void* packed,
                           const float* alpha, float* y, int64_t M, int64_t N,
                           int64_t K, void* workspace, size_t workspace_bytes,
@@ -269,8 +268,8 @@ sherry_status sherry_linear_plan(int64_t M, int64_t N, int64_t K, int* path,
  *          0 (or a value the path does not take) = built-in choice.
  *   ch     path 0: k-tiles (128 inputs) per LDS table stage: 1, 2, 4
  *          or 8, capped so one stage stays within 32 KB;
- *          path 1 (forced) with 64-token tiles: 2 or 4 k-phases (4: tiles
- *          128 weight rows wide, each workgroup's K split four ways);
+ *          path 1 (forced): 2 or 4 k-phases (4: tiles 128 weight rows
+ *          wide, each workgroup's K split four ways);
  *          0 = built-in.
  *   splits K-splits per output row group; 0 = built-in choice.
  * Results do not depend on the plan.  sherry_workspace_bytes reflects the

@@ -100,24 +100,25 @@ def test_plan_dispatch_rule():
 
 
 def test_prefill_tile_height_rule():
-    """The prefill GEMM takes tiles of 64 tokens when that grid fits the GPU
-    in one round (<= 256 tiles of 256 weight rows), else 128; with 64-token
-    tiles it takes 4 k-phases (tiles of 128 weight rows) when that doubled
-    grid still fits, else 2.  Between 65 and 128 tokens it is the default,
-    except at M <= 88 on a grid under 128 workgroups with more than 16
-    k-tiles per wave, where the 64-token GEMV launches stay."""
-    lds64, lds64kp4, lds128 = 78080, 106752, 107016   # the three kernels' LDS per workgroup
+    """The prefill GEMM takes the first tile shape whose grid fits the GPU in
+    one round (<= 256 tiles): 64 tokens x 128 weight rows (4 k-phases), then
+    128 x 128 (4 k-phases), then 64 x 256 (2 k-phases), else 128 x 256
+    (2 k-phases).  Between 65 and 128 tokens it is the default, except at
+    M <= 88 on a grid under 128 workgroups with more than 16 k-tiles per
+    wave, where the 64-token GEMV launches stay."""
+    # LDS per workgroup of the four kernels, by (tokens, weight rows)
+    lds = {(64, 256): 78080, (64, 128): 106752, (128, 256): 107016, (128, 128): 139792}
     def tiles(M, N, bm, bn):
         return -(-M // bm) * -(-N // bn)
     for M, N in [(129, 14336), (200, 14336), (256, 14336), (257, 14336), (512, 14336),
-                 (128, 4096), (136, 4096), (300, 4096), (1000, 4096), (1100, 4096), (129, 65536)]:
+                 (128, 4096), (136, 4096), (300, 4096), (1000, 4096), (1100, 4096), (129, 65536),
+                 (129, 28672), (384, 8192)]:
         p = bw.plan(M, N, 4096)
         assert p["path"] == "decode_mfma"
-        want64 = tiles(M, N, 64, 256) <= 256
-        kp4 = want64 and tiles(M, N, 64, 128) <= 256
-        assert p["lds_bytes"] == (lds64kp4 if kp4 else lds64 if want64 else lds128), (M, N)
-        nt = -(-N // (128 if kp4 else 256))
-        assert p["grid"] == 8 * -(-nt // 8) * -(-M // (64 if want64 else 128)), (M, N)
+        bm, bn = next((s for s in ((64, 128), (128, 128), (64, 256)) if tiles(M, N, *s) <= 256),
+                      (128, 256))
+        assert p["lds_bytes"] == lds[(bm, bn)], (M, N)
+        assert p["grid"] == 8 * -(-(-(-N // bn)) // 8) * -(-M // bm), (M, N)
     # 64 < M <= 128: the prefill, but the GEMV launches on a small grid with long K at M <= 88
     for M, N, K, want in [(65, 14336, 4096, "decode_mfma"), (96, 14336, 4096, "decode_mfma"),
                           (128, 14336, 4096, "decode_mfma"), (65, 4096, 4096, "decode_mfma"),
@@ -347,8 +348,9 @@ def test_plan_invariants_over_random_shapes():
         ws = bw.workspace_bytes(M, N, K)
         if p["path"] == "decode_mfma":
             assert p["splits"] == 1 and ws == 0
-            # 64-token tiles (2 or 4 k-phases: 256- or 128-row tiles) or 128-token tiles
-            bm, bn = {78080: (64, 256), 106752: (64, 128), 107016: (128, 256)}[p["lds_bytes"]]
+            # 64- or 128-token tiles of 256 or 128 weight rows (2 or 4 k-phases)
+            bm, bn = {78080: (64, 256), 106752: (64, 128), 107016: (128, 256),
+                      139792: (128, 128)}[p["lds_bytes"]]
             assert p["grid"] == 8 * -(-(-(-N // bn)) // 8) * -(-M // bm), (M, N, K, p)
             # 4 k-phases only when the real tiles (the grid less its XCD padding) fit one round
             assert -(-M // bm) * -(-N // bn) <= 256 or bn == 256, (M, N, K, p)

@@ -337,13 +337,13 @@ def test_linear_fused_unsplit_long_waves(orc, rw, K, M):
     assert_y_close(gl.cpu().numpy(), y)
 
 
-@pytest.mark.parametrize("bm,kp", [(1, 2), (1, 4), (2, 0)])  # 64-token tiles, 2 or 4 k-phases; 128
+@pytest.mark.parametrize("bm,kp", [(1, 2), (1, 4), (2, 2), (2, 4)])  # 64- / 128-token tiles, 2 / 4 k-phases
 @pytest.mark.parametrize("M", [1, 7, 16, 17, 40, 64, 65, 100, 128, 129, 200, 300])
 def test_gemm_prefill_kernel_at_small_m(orc, packed_cases, M, bm, kp):
     """The prefill kernel forced onto small and mid M with either tile height
-    and, for 64-token tiles, 2 or 4 k-phases (rows past M clamped, a ragged
-    last token tile, N = 320 ragged against 128- and 256-row tiles, 9
-    k-tiles: a short last step with 2 and with 4 phases)."""
+    and 2 or 4 k-phases (rows past M clamped, a ragged last token tile,
+    N = 320 ragged against 128- and 256-row tiles, 9 k-tiles: a short last
+    step with 2 and with 4 phases)."""
     N, K = 320, 1152
     T, alpha, packed, galpha = packed_cases[(N, K)]
     q = synth.int8_uniform(M, K, seed=2900 + M)
@@ -448,7 +448,7 @@ def workload_5_ref(orc):
     return w, acc, y, packed, galpha, gq, gs
 
 
-@pytest.mark.parametrize("bm,kp", [(0, 0), (1, 2), (1, 4), (2, 0)])  # built-in, or forced tiles / k-phases
+@pytest.mark.parametrize("bm,kp", [(0, 0), (1, 2), (1, 4), (2, 2), (2, 4)])  # built-in, or forced tiles / k-phases
 def test_workload_5_prefill_full(workload_5_ref, bm, kp):
     """Every one of the 7.3 M outputs of workload 5: int32 bit-exact, fp32
     within 1e-5 (bit-identical in practice)."""
@@ -489,7 +489,8 @@ def test_random_shapes_every_path(orc, M, N, K):
     packed, galpha = gpu_pack(W)
     assert np.array_equal(packed.cpu().numpy(), orc.pack(T)), "packed codes"
     gq, gs = bw.quantize_act(x.cuda())
-    paths = [(None, 0, 0), ("decode_mfma", 1, 2), ("decode_mfma", 1, 4), ("decode_mfma", 2, 0)]
+    paths = [(None, 0, 0), ("decode_mfma", 1, 2), ("decode_mfma", 1, 4), ("decode_mfma", 2, 2),
+             ("decode_mfma", 2, 4)]
     if M <= 16:
         paths += [("lut_gemv", 0, 0), ("decode_mfma_gemv", 0, 0)]
     elif M <= 128:
