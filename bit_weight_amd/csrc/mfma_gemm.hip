@@ -26,7 +26,7 @@
 //    j+2 starts right after the barrier of step j, once every wave is done
 //    with the buffer it overwrites, and has two steps to land (two buffers
 //    and one step with BM = 128 and 4 phases, whose 12 x 16 KB would not
-//    fit LDS);
+//    fit LDS; with BM = 64 four buffers and one barrier per two steps);
 //  * weights: each wave decodes exactly the B operands it consumes.  It loads
 //    its row tile's 1280-byte k-tile coalesced (lane l = slot l, 16 + 4
 //    bytes), which by the format's design already holds, for column block t,
@@ -64,10 +64,15 @@ constexpr int kThreads = 512;                   // 8 waves: row tiles x k-phases
 template <int BM, int KP>
 struct Tiling {
   static_assert(KP == 2 || KP == 4, "k-phases: 2 or 4");
-  // activation buffers per k-phase: three (the copy for step j+2 issued in
-  // step j), or two with 128-row tiles and 4 phases, whose 4 x 3 x 16 KB
-  // would not fit LDS (the copy for step j+1 issued in step j)
-  static constexpr int kABufs = BM == 128 && KP == 4 ? 2 : 3;
+  // 64-row tiles: one barrier per two k-steps, four activation buffers per
+  // k-phase, the copies for steps j+2 and j+3 issued in step j (measured at
+  // K=4096: M=128, N=14336 14.5 -> 13.6 us; M=320, N=11008 20.9 -> 20.5;
+  // no faster with 128-row tiles).  Else a barrier per k-step with three
+  // buffers (the copy for step j+2 issued in step j), or two with 128-row
+  // tiles and 4 phases, whose 4 x 3 x 16 KB would not fit LDS (the copy for
+  // step j+1 issued in step j).
+  static constexpr bool kPair = BM == 64;
+  static constexpr int kABufs = kPair ? 4 : (BM == 128 && KP == 4 ? 2 : 3);
   static constexpr int kRT = kThreads / 64 / KP;       // row tiles per workgroup (4 or 2)
   static constexpr int kBN = kRT * kTileRows;          // workgroup tile width (256 or 128 weight rows)
   static constexpr int kOutLd = kBN + 16;              // words per row of the epilogue tiles (the 4
@@ -82,8 +87,10 @@ struct Tiling {
   // vector-memory ops a wave issues between a k-step's activation copy and
   // that step's barrier: with three buffers the codes three steps ahead of
   // it (2), the next step's copy, and the codes four steps ahead (2); with
-  // two, the codes two steps ahead of it (2)
-  static constexpr int kNewerLoads = kABufs == 3 ? 2 + kACopies + 2 : 2;
+  // two, the codes two steps ahead of it (2); with a barrier per two steps
+  // (the copy of steps j, j+1 issued at step j-2), the codes of steps j+1
+  // and j+2 (2 + 2)
+  static constexpr int kNewerLoads = kPair ? 4 : (kABufs == 3 ? 2 + kACopies + 2 : 2);
 };
 
 // Activation tile in LDS, row-major with 128-byte rows: the 16-byte chunk c
@@ -181,6 +188,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   constexpr int kBM = BM, kMT = T::kMT, kAStage = T::kAStage, kACopies = T::kACopies;
   constexpr int kLdsBytes = T::kLdsBytes, kNewerLoads = T::kNewerLoads;
   constexpr int kRT = T::kRT, kBN = T::kBN, kOutLd = T::kOutLd, kABufs = T::kABufs;
+  constexpr bool kPair = T::kPair;
   // the activation buffers [buffer][phase]; after the main loop the
   // epilogue tile reuses them
   // (32-bit words: every view below is a character type or 32-bit lanes)
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   // The arrival and the polls are LDS instructions in asm: as built-ins the
   // compiler cannot tell them from the activation copies in flight and waits
   // for those first.  The poll is bounded (~0.3 s), so a wave always leaves.
-  auto parity_barrier = [&](int j) {
+  auto parity_barrier = [&](int j) {   // j: the barrier's index
     const uint32_t pa = (uint32_t)(size_t)((__attribute__((address_space(3))) unsigned*)&parity_arrivals[kh]);
     if (lane == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(pa), "v"(1u) : "memory");
     const unsigned target = (unsigned)kRT * (unsigned)(j + 1);
@@ -322,24 +330,33 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
       __builtin_amdgcn_s_sleep(1);
     }
   };
-  auto step = [&](int j, int b, v4u& wn, uint32_t& hn, const v4i (&bc0)[kNT], const v4i (&bc1)[kNT],
-                  v4i (&bn0)[kNT], v4i (&bn1)[kNT]) {
-    // every wave's copy of step j has landed and its earlier LDS reads are
-    // done; then the buffer of step j-1 is free for the copy of step j+2
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kNewerLoads));
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (BM == 128)
-      parity_barrier(j);
-    else
-      __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kABufs == 3)
-      copy_a(min(j + 2, KJ - 1), b == 0 ? 2 : b - 1);
-    else
-      copy_a(min(j + 1, KJ - 1), b ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
+  // `even`: j is even (a constant at every call), so with a barrier per two
+  // steps the odd steps fold to the decode and the MFMAs.
+  auto step = [&](int j, int b, bool even, v4u& wn, uint32_t& hn, const v4i (&bc0)[kNT],
+                  const v4i (&bc1)[kNT], v4i (&bn0)[kNT], v4i (&bn1)[kNT]) {
+    // every wave's copy of step j (and j+1) has landed and its earlier LDS
+    // reads are done; then the buffer of step j-1 is free for the copy of
+    // step j+2 (those of j-2, j-1 for j+2, j+3)
+    if (!kPair || even) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kNewerLoads));
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (BM == 128)
+        parity_barrier(j);
+      else
+        __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kPair) {
+        copy_a(min(j + 2, KJ - 1), (b + 2) & 3);
+        copy_a(min(j + 3, KJ - 1), (b + 3) & 3);
+      } else if constexpr (kABufs == 3) {
+        copy_a(min(j + 2, KJ - 1), b == 0 ? 2 : b - 1);
+      } else {
+        copy_a(min(j + 1, KJ - 1), b ^ 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     uint32_t f0[kNT], f1[kNT];
     split(wn, hn, f0, f1);
     load_codes(min(j + 3, KJ - 1), wn, hn);
@@ -353,7 +370,10 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   // Two register stages of codes and two sets of B operands, ping-pong.
   // Issue order (the barrier's vmcnt counts on it): codes 0, copy 0,
   // codes 1, copy 1 (three buffers only), codes 2, then per step j:
-  // barrier, copy j+2 (j+1 with two buffers), codes j+3.
+  // barrier, copy j+2 (j+1 with two buffers), codes j+3.  With a barrier
+  // per two steps: codes 0, copy 0, copy 1, codes 1, codes 2, then per
+  // even step j: barrier, copies j+2 and j+3, codes j+3; per odd step:
+  // codes j+3.
   v4u w0, w1;
   uint32_t h0, h1;
   v4i bA0[kNT], bA1[kNT], bB0[kNT], bB1[kNT];
@@ -361,9 +381,13 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   __builtin_amdgcn_sched_barrier(0);
   copy_a(0, 0);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kPair) {
+    copy_a(min(1, KJ - 1), 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   load_codes(min(1, KJ - 1), w1, h1);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kABufs == 3) copy_a(min(1, KJ - 1), 1);
+  if constexpr (!kPair && kABufs == 3) copy_a(min(1, KJ - 1), 1);
   __builtin_amdgcn_sched_barrier(0);
   // decode table written (LDS only: the copies stay in flight)
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
@@ -384,12 +408,12 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
 
   int j = 0, b = 0;
   for (; j + 2 <= KJ; j += 2) {
-    step(j, b, w1, h1, bA0, bA1, bB0, bB1);
+    step(j, b, true, w1, h1, bA0, bA1, bB0, bB1);
     b = b + 1 == kABufs ? 0 : b + 1;
-    step(j + 1, b, w0, h0, bB0, bB1, bA0, bA1);
+    step(j + 1, b, false, w0, h0, bB0, bB1, bA0, bA1);
     b = b + 1 == kABufs ? 0 : b + 1;
   }
-  if (j < KJ) step(j, b, w1, h1, bA0, bA1, bB0, bB1);
+  if (j < KJ) step(j, b, true, w1, h1, bA0, bA1, bB0, bB1);
   // the clamped copies past the end may still be landing in LDS, which the
   // epilogue reuses
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));

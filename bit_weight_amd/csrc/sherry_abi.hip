@@ -83,7 +83,12 @@ GemmPlan plan_mfma_gemv(int M, int N, int K) {
       splits = (KT + per_split - 1) / per_split;
     }
   } else if (M > 8) {
-    splits = (2 * KT + 3 * kw) / (6 * kw);   // KT / (3 kw), rounded
+    // KT / (3 kw), rounded, but no more workgroups than one round of CUs: a
+    // second, partial round costs a whole wave of launches (measured at
+    // N=4096, K=14336: 5 splits, 320 workgroups, M=17 13.9 us, M=64 25.0;
+    // 4 splits 9.2 and 15.8)
+    splits = (2 * KT + 3 * kw) / (6 * kw);
+    if (splits * RT > kCUs) splits = kCUs / RT;
     if (splits < 1) splits = 1;
   } else {
     const int by_waves = (1024 + RT * kw - 1) / (RT * kw);
@@ -178,14 +183,14 @@ GemmPlan plan_prefill(int M, int N, int K) {
   const long long mt64 = (M + 63) / 64, mt128 = (M + 127) / 128;
   const long long nt128 = (N + 127) / 128, nt256 = (N + 255) / 256;
   int bm = 128, kp = 2;
-  if (mt64 * nt128 <= 256) bm = 64, kp = 4;
-  else if (mt128 * nt128 <= 256) bm = 128, kp = 4;
-  else if (mt64 * nt256 <= 256) bm = 64, kp = 2;
+  if (mt64 * nt128 <= kCUs) bm = 64, kp = 4;
+  else if (mt128 * nt128 <= kCUs) bm = 128, kp = 4;
+  else if (mt64 * nt256 <= kCUs) bm = 64, kp = 2;
   const int ovr_rw = g_ovr_rw.load();
   const bool forced = g_ovr_path.load() == 1;
   if (forced && (ovr_rw == 1 || ovr_rw == 2)) {
     bm = 64 * ovr_rw;
-    kp = (bm == 64 ? mt64 : mt128) * nt128 <= 256 ? 4 : 2;
+    kp = (bm == 64 ? mt64 : mt128) * nt128 <= kCUs ? 4 : 2;
   }
   const int ovr_ch = g_ovr_ch.load();
   if (forced && (ovr_ch == 2 || ovr_ch == 4)) kp = ovr_ch;
@@ -204,14 +209,28 @@ GemmPlan plan_prefill(int M, int N, int K) {
 
 // M <= 16: the built-in small-M path (or the override's); 16 < M <= 64: the
 // matrix-core GEMV unless the prefill kernel is forced; 64 < M <= 128: the
-// prefill kernel, except at M <= 88 on a grid of fewer than 128 workgroups
-// whose waves each take more than 16 k-tiles, where the same GEMV in
-// launches of 64 tokens (each streaming the weights again) is faster
-// (measured, us, GEMV launches against prefill: N=14336, K=4096 M=65
-// 15.6/14.3, M=128 22.0/14.5; N=4096, K=4096 M=65 15.0/13.9; N=28672,
-// K=8192 M=65 41.0/39.2; N=4096, K=14336 M=65 30.0/36.5, M=80 33.4/36.5,
-// M=96 40.0/36.4);
+// prefill kernel, except on a prefill grid of at most 64 workgroups whose
+// waves take long shares of K (chunk_max_m), where the same GEMV in
+// launches of 64 tokens (each streaming the weights again) is faster; wider
+// grids keep the prefill (N=14336, K=4096 M=65 15.6 against 13.1 us;
+// N=5504, K=8192 M=72 21.3 against 20.9);
 // M > 128: prefill.
+// 64 < M <= 128 on a prefill grid of at most 64 workgroups (N <= 4096):
+// the most tokens for which the GEMV in launches of 64 tokens beats the
+// prefill, by the prefill's k-tiles per wave (one round, so its time grows
+// with them).  From sweeps of M = 65..128 step 8 (us, GEMV launches against
+// the prefill's 64 x 128 tiles): N=4096, K=14336 (28 k-tiles per wave)
+// 19.9 / 32.4 at M=65, 29.8 / 33.1 at M=128; K=11008 (22) 23.5 / 26.5 at
+// M=96, 26.6 / 26.7 at M=104; K=8192 (16) 19.3 / 20.7 at M=80, 21.5 / 20.7
+// at M=88; N=1024, K=8192 (16) 18.1 / 20.6 at M=80; K=4096 (8) 15.1 / 12.9
+// at M=65.
+int chunk_max_m(int kt_per_wave) {
+  if (kt_per_wave <= 12) return kGemvMaxM;
+  if (kt_per_wave <= 18) return 80;
+  if (kt_per_wave <= 24) return 96;
+  return kChunkMaxM;
+}
+
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   const int ovr = g_ovr_path.load();
@@ -219,8 +238,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
   if (M > kGemvMaxM) {
     const GemmPlan pf = plan_prefill(M, N, K);
     const int kt_per_wave = (k_tiles(K) + pf.ch - 1) / pf.ch;
-    if (ovr < 0 && (M > kChunkPrefillM || pf.grid >= kPrefillMinGrid || kt_per_wave <= kPrefillMaxKtPerWave))
-      return pf;
+    if (ovr < 0 && (pf.grid > kChunkMaxGrid || M > chunk_max_m(kt_per_wave))) return pf;
     GemmPlan c = plan_mfma_gemv(kGemvMaxM, N, K);
     c.chunk = kGemvMaxM;
     return c;

@@ -26,11 +26,11 @@ struct GemmPlan {
 
 constexpr int kLutMaxM = 16;          // M <= 16 takes a GEMV path
 constexpr int kGemvMaxM = 64;         // 16 < M <= 64: the matrix-core GEMV, unless path 1 is forced
-constexpr int kChunkMaxM = 128;       // 64 < M <= 128: the prefill GEMM, unless at most 88
-constexpr int kChunkPrefillM = 88;    //   tokens, a grid under 128 workgroups and more than
-constexpr int kPrefillMinGrid = 128;  //   16 k-tiles per wave: then the GEMV in launches of
-constexpr int kPrefillMaxKtPerWave = 16;  // 64 tokens
+constexpr int kChunkMaxM = 128;       // 64 < M <= 128: the prefill GEMM, or the GEMV in
+constexpr int kChunkMaxGrid = 64;     //   launches of 64 tokens where the prefill grid is at
+                                      //   most 64 workgroups (chunk_max_m)
 constexpr int kGemvWaves = 4;         // waves per GEMV workgroup
+constexpr int kCUs = 256;             // MI355X compute units: one round of one workgroup each
 constexpr int kDefaultSmallMPath = 2;  // M <= 16: 0 = lookup tables, 2 = matrix-core GEMV
 constexpr int kFuseMaxM = 4;           // fused quantization: at most 4 tokens,
 constexpr int kFuseMaxMK = 16384;      //   M*K elements read per workgroup for the scales,

@@ -134,10 +134,12 @@ sherry_status sherry_quantize_act(const float* x, int64_t M, int64_t K,
  *            block and token pair);
  *   16 < M <= 64: the matrix-core GEMV with the tokens in two or four
  *            blocks of 16;
- *   64 < M <= 128: the prefill GEMM below, except at M <= 88 when its
- *            grid is under 128 workgroups and each wave would take more
- *            than 16 k-tiles: then that GEMV in launches of 64 tokens on
- *            the same stream (sherry_workspace_bytes covers one launch);
+ *   64 < M <= 128: the prefill GEMM below, except when its grid is at
+ *            most 64 workgroups and its waves take long shares of K (more
+ *            than 12 k-tiles each up to M = 80, more than 18 up to 96,
+ *            more than 24 up to 128): then that GEMV in launches of 64
+ *            tokens on the same stream (sherry_workspace_bytes covers one
+ *            launch);
  *   M > 128: the prefill GEMM on the int8 matrix cores, in the first
  *            workgroup tile whose grid fits the GPU in one round (at most
  *            256 tiles): 64 tokens x 128 weight rows, 128 x 128, 64 x 256,

@@ -103,11 +103,12 @@ def test_prefill_tile_height_rule():
     """The prefill GEMM takes the first tile shape whose grid fits the GPU in
     one round (<= 256 tiles): 64 tokens x 128 weight rows (4 k-phases), then
     128 x 128 (4 k-phases), then 64 x 256 (2 k-phases), else 128 x 256
-    (2 k-phases).  Between 65 and 128 tokens it is the default, except at
-    M <= 88 on a grid under 128 workgroups with more than 16 k-tiles per
-    wave, where the 64-token GEMV launches stay."""
+    (2 k-phases).  Between 65 and 128 tokens it is the default, except on a
+    prefill grid of at most 64 workgroups whose waves take more than 12
+    k-tiles (up to M = 80), 18 (up to 96) or 24 (up to 128): there the
+    64-token GEMV launches stay."""
     # LDS per workgroup of the four kernels, by (tokens, weight rows)
-    lds = {(64, 256): 78080, (64, 128): 106752, (128, 256): 107016, (128, 128): 139792}
+    lds = {(64, 256): 78080, (64, 128): 139520, (128, 256): 107016, (128, 128): 139792}
     def tiles(M, N, bm, bn):
         return -(-M // bm) * -(-N // bn)
     for M, N in [(129, 14336), (200, 14336), (256, 14336), (257, 14336), (512, 14336),
@@ -119,13 +120,16 @@ def test_prefill_tile_height_rule():
                       (128, 256))
         assert p["lds_bytes"] == lds[(bm, bn)], (M, N)
         assert p["grid"] == 8 * -(-(-(-N // bn)) // 8) * -(-M // bm), (M, N)
-    # 64 < M <= 128: the prefill, but the GEMV launches on a small grid with long K at M <= 88
+    # 64 < M <= 128: the prefill, but the GEMV launches on a small grid with long K
     for M, N, K, want in [(65, 14336, 4096, "decode_mfma"), (96, 14336, 4096, "decode_mfma"),
                           (128, 14336, 4096, "decode_mfma"), (65, 4096, 4096, "decode_mfma"),
                           (100, 4096, 4096, "decode_mfma"), (65, 28672, 8192, "decode_mfma"),
                           (80, 4096, 14336, "decode_mfma_gemv"), (88, 4096, 14336, "decode_mfma_gemv"),
-                          (89, 4096, 14336, "decode_mfma"), (65, 1024, 8192, "decode_mfma"),
-                          (65, 1024, 8448, "decode_mfma_gemv")]:
+                          (128, 4096, 14336, "decode_mfma_gemv"), (96, 4096, 11008, "decode_mfma_gemv"),
+                          (97, 4096, 11008, "decode_mfma"), (80, 4096, 8192, "decode_mfma_gemv"),
+                          (81, 4096, 8192, "decode_mfma"), (65, 4096, 6144, "decode_mfma"),
+                          (65, 4096, 6272, "decode_mfma_gemv"), (65, 5504, 8192, "decode_mfma"),
+                          (65, 1024, 8192, "decode_mfma_gemv"), (88, 1024, 8192, "decode_mfma")]:
         assert bw.plan(M, N, K)["path"] == want, (M, N, K)
 
 
@@ -343,13 +347,13 @@ def test_plan_invariants_over_random_shapes():
             assert p["path"] in ("lut_gemv", "decode_mfma_gemv"), (M, N, K, p)
         elif M <= 64:
             assert p["path"] == "decode_mfma_gemv", (M, N, K, p)
-        elif M > 88:
+        elif M > 128 or -(-N // 128) > 32:   # past M = 128, or a prefill grid over 64
             assert p["path"] == "decode_mfma", (M, N, K, p)
         ws = bw.workspace_bytes(M, N, K)
         if p["path"] == "decode_mfma":
             assert p["splits"] == 1 and ws == 0
             # 64- or 128-token tiles of 256 or 128 weight rows (2 or 4 k-phases)
-            bm, bn = {78080: (64, 256), 106752: (64, 128), 107016: (128, 256),
+            bm, bn = {78080: (64, 256), 139520: (64, 128), 107016: (128, 256),
                       139792: (128, 128)}[p["lds_bytes"]]
             assert p["grid"] == 8 * -(-(-(-N // bn)) // 8) * -(-M // bm), (M, N, K, p)
             # 4 k-phases only when the real tiles (the grid less its XCD padding) fit one round

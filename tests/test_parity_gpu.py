@@ -518,14 +518,16 @@ def test_random_shapes_every_path(orc, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 8192, 28672), (8, 8192, 28672), (16, 8192, 28672),
                                    (9, 4096, 4096), (16, 4096, 11008), (64, 4096, 4096),
-                                   (88, 4096, 14336)])
+                                   (88, 4096, 14336), (128, 4096, 14336), (64, 4096, 14336),
+                                   (40, 5504, 8192)])
 def test_gemm_gemv_plan_rule_shapes(orc, M, N, K):
     """The GEMV plans the built-in rule picks at these shapes: K split at
     wide N and long K for one token block (a wave keeps at most 8 or 16
     k-tiles), and 8 waves per row tile with few splits above 8 tokens at
-    narrow N (one split at K=4096; launches of 64 + 24 tokens at M=88,
-    K=14336, where the prefill's grid is small and its waves' K long): y and
-    the int32 sums against the oracle."""
+    narrow N (one split at K=4096; no more workgroups than CUs: 4 splits at
+    N=4096, K=14336, 2 at N=5504, K=8192; launches of 64 + 24 and 64 + 64
+    tokens at M=88 and 128, K=14336, where the prefill's grid is small and
+    its waves' K long): y and the int32 sums against the oracle."""
     W = synth.weights(N, K, 0.02, False, seed=9300 + N + K)
     x = synth.activations(M, K, seed=9400 + M + K)
     T, alpha = orc.quantize(W.numpy())
@@ -541,7 +543,7 @@ def test_gemm_gemv_plan_rule_shapes(orc, M, N, K):
         per_wave = -(-(-(-KT // p["splits"])) // (p["block"] // 64))
         assert p["splits"] > 1 and per_wave <= (16 if M > 8 else 8), p
     if RT < 128 and M > 8:
-        assert p["block"] == 512, p
+        assert p["block"] == 512 and p["grid"] <= 256, p
     ws = torch.zeros(max(bw.workspace_bytes(M, N, K), 256), dtype=torch.uint8, device="cuda")
     gy = bw.gemm(gq, gs, packed, galpha, N, K, workspace=ws)
     gacc = bw.gemm_i32(gq, packed, N, K, workspace=ws)
