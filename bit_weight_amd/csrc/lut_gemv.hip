@@ -6,9 +6,9 @@
 // results are summed in integers, with one float rescale at the end.
 //
 // Mapping on gfx950 (wave64):
-//  * A workgroup has RW x KW waves: RW format row tiles (64 output rows each,
-//    one row per lane) times KW waves that share a row tile and take turns
-//    over its k-tiles.  It covers the k-tiles of one K-split in stages of CH
+//  * A workgroup has RW x KW waves (4, or 8 as 4 x 2): RW format row tiles
+//    (64 output rows each, one row per lane) times KW waves that share a row
+//    tile and take turns over its k-tiles.  It covers the k-tiles of one K-split in stages of CH
 //    k-tiles (128 inputs each); the tables of one stage live in LDS.
 //  * Each lane streams one slot of the tile, 16 + 4 bytes per k-tile, both
 //    loads coalesced across the wave; the next stage's codes are requested
@@ -286,6 +286,13 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
 
 template <int MP, int CH, int RW, int KW, bool FQ>
 hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  // the tables of a stage can take all of the first 64 KB of LDS, which
+  // with the kernel's static arrays needs the larger dynamic limit
+  if (p.lds_bytes + 1024 > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(lut_gemv_kernel<MP, CH, RW, KW, FQ>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes + 1024);
+    if (e != hipSuccess) return e;
+  }
   launch_product_kernel(lut_gemv_kernel<MP, CH, RW, KW, FQ>, dim3(p.grid), dim3(64 * RW * KW), p.lds_bytes,
                      stream, a, p.splits, p.kt_per_split);
   return hipGetLastError();
@@ -297,6 +304,8 @@ hipError_t launch_ch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     case 4: return launch_cfg<MP, CH, 4, 1, FQ>(p, a, stream);
     case 2: return launch_cfg<MP, CH, 2, 2, FQ>(p, a, stream);
     case 1: return launch_cfg<MP, CH, 1, 4, FQ>(p, a, stream);
+    // 8 waves: 4 row tiles x 2 waves that take turns over a stage's k-tiles
+    case 8: if constexpr (CH >= 2) return launch_cfg<MP, CH, 4, 2, FQ>(p, a, stream); break;
     default: return hipErrorInvalidValue;
   }
 }

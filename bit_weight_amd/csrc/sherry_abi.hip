@@ -255,37 +255,44 @@ GemmPlan plan_gemm(int M, int N, int K) {
 
   // Built-in plan from sweeps of row tiles per workgroup x table stage x
   // K-splits on MI355X (M = 1..16 at N = 4096..28672, K = 4096..11008):
-  // row tiles per workgroup (its 4 waves are rw row tiles x 4/rw waves
-  // sharing one): up to 4 tokens 1, or 2 from 128 row tiles; up to 8
-  // tokens 2; above 8 tokens 4; and 4 from 448 row tiles.  K-splits of 2
-  // k-tiles for 1-2 tokens, and above 8 tokens below 128 row tiles, of 8
-  // above 8 tokens from 448 row tiles, else 4, at most 16 splits: more
-  // workgroups keep more lookups in flight, and the 64-bit cell atomics of
-  // the splits cost less than idle CUs.  One k-tile per table stage with 4
-  // row tiles, else the largest stage that fits.  Measured against the
-  // earlier rule (1 or 4 row tiles, stages as large as fit, 2-k-tile splits
-  // above 8 tokens), us: M=8 at N=28672, K=8192 39.3 -> 34.0; M=6 there
-  // 40.1 -> 26.7; M=16 there 70.0 -> 60.0; M=1 there 17.3 -> 14.3; M=8 at
-  // N=K=4096 12.9 -> 9.9; M=12 at N=14336, K=4096 27.0 -> 22.0; M=1 at
-  // N=14336, K=4096 7.3 -> 6.2; M=4 at N=11008 10.8 -> 9.4.
-  const int rw_def = RT >= 448 || M > 8 ? 4 : M > 4 ? 2 : RT >= 128 ? 2 : 1;
+  // row tiles per workgroup (rw = 1, 2 or 4 row tiles of 4 / rw waves
+  // each, or rw = 8: 4 row tiles of 2 waves): up to 4 tokens 1, or 2 from
+  // 128 row tiles, and 4 from 448 row tiles; above 4 tokens 8.  K-splits of
+  // 2 k-tiles for 1-2 tokens, 4 for 3-4 tokens; above 4 tokens 2 below 128
+  // row tiles, 8 from 448, else 4; at most 16 splits: more workgroups keep
+  // more lookups in flight, and the 64-bit cell atomics of the splits cost
+  // less than idle CUs.  Table stages of one k-tile with 4 row tiles of one
+  // wave, two with two waves (one k-tile each), else the largest stage that
+  // fits.  Measured against the earlier rule (1 or 4 row tiles, stages as
+  // large as fit, 2-k-tile splits above 8 tokens), us: M=8 at N=28672,
+  // K=8192 39.3 -> 34.0; M=6 there 40.1 -> 26.7; M=16 there 70.0 -> 60.0;
+  // M=1 there 17.3 -> 14.3; M=8 at N=K=4096 12.9 -> 9.9; M=12 at N=14336,
+  // K=4096 27.0 -> 22.0; M=1 at N=14336, K=4096 7.3 -> 6.2; M=4 at N=11008
+  // 10.8 -> 9.4.  The 8-wave form against 4 row tiles of one wave (2 to 4
+  // row tiles above 4 tokens before), us: M=8 at N=28672, K=8192 33.8 ->
+  // 29.2; M=16 at N=K=4096 17.3 -> 16.6; M=12 there 13.7 -> 11.6; M=8
+  // there 10.1 -> 9.3; M=16 at N=14336 28.3 -> 27.4, at K=11008 29.2 ->
+  // 27.3; at M=4 it was slower (6.0 against 6.3).
+  const int rw_def = M > 4 ? 8 : RT >= 448 ? 4 : RT >= 128 ? 2 : 1;
   int rw = g_ovr_rw.load() > 0 ? g_ovr_rw.load() : rw_def;
-  if (rw != 1 && rw != 2 && rw != 4) rw = 4;
-  const int G = (RT + rw - 1) / rw;
-  const int kt_per_split_def = M <= 2 ? 2 : M <= 8 ? 4 : RT < 128 ? 2 : RT < 448 ? 4 : 8;
+  if (rw != 1 && rw != 2 && rw != 4 && rw != 8) rw = 4;
+  const int kt_per_split_def = M <= 2 ? 2 : M <= 4 ? 4 : RT < 128 ? 2 : RT < 448 ? 4 : 8;
   int splits = g_ovr_splits.load() > 0 ? g_ovr_splits.load() : KT / kt_per_split_def;
   if (splits > 16 && g_ovr_splits.load() <= 0) splits = 16;
   if (splits > KT) splits = KT;
   if (splits < 1) splits = 1;
   const int kt_per_split = (KT + splits - 1) / splits;
   splits = (KT + kt_per_split - 1) / kt_per_split;
-  int ch = 1;
-  const int ch_cap = g_ovr_ch.load() > 0 ? g_ovr_ch.load() : (rw == 4 ? 1 : ch_max);
+  if (rw == 8 && kt_per_split < 2) rw = 4;   // two waves need a stage of two k-tiles
+  const int rtw = rw == 8 ? 4 : rw;          // row tiles per workgroup
+  const int kw = rw == 8 ? 2 : kGemvWaves / rw;   // waves per row tile
+  const int G = (RT + rtw - 1) / rtw;
+  int ch = rw == 8 ? 2 : 1;
+  const int ch_cap = g_ovr_ch.load() > 0 ? g_ovr_ch.load() : (rw == 4 || rw == 8 ? ch : ch_max);
   while (ch * 2 <= ch_cap && ch * 2 <= ch_max && ch * 2 <= kt_per_split) ch *= 2;
 
-  const int kw = kGemvWaves / rw;
   const int lut_bytes = ch * 32 * MP * 32 * 4;
-  const int red_bytes = (kw - 1) * 2 * MP * rw * 64 * 4;
+  const int red_bytes = (kw - 1) * 2 * MP * rtw * 64 * 4;
   p.path = 0;
   p.groups = G;
   p.rw = rw;
@@ -293,7 +300,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
   p.splits = splits;
   p.kt_per_split = kt_per_split;
   p.grid = G * splits;
-  p.block = 64 * kGemvWaves;
+  p.block = 64 * rtw * kw;
   p.lds_bytes = lut_bytes > red_bytes ? lut_bytes : red_bytes;
   p.ws_bytes = splits > 1 ? (size_t)M * N * sizeof(unsigned long long) : 0;
   return p;

@@ -234,7 +234,8 @@ sherry_status sherry_gemm2(const int8_t* x, const float* s_x, const void* packed
 /* Launch plan sherry_gemm uses for a shape (host-only, pure; for
  * diagnostics and benchmarks).  Any output pointer may be NULL.
  *   path: 0 = lookup-table GEMV (per-segment tables in LDS, §2.2; M <= 16),
- *         1 = decode + int8 matrix-core GEMM (M > 128, and M > 96 for wide N),
+ *         1 = decode + int8 matrix-core GEMM (M > 64, except where path 2
+ *             runs in launches of 64 tokens),
  *         2 = decode + int8 matrix-core GEMV (M <= 128; grid is per launch
  *             of at most 64 tokens).
  *   grid: workgroups per launch; block: threads per workgroup;
@@ -263,13 +264,16 @@ sherry_status sherry_linear_plan(int64_t M, int64_t N, int64_t K, int* path,
  *   path   -1 = built-in choice, or 0, 1, 2 as in sherry_gemm_plan; for
  *          16 < M <= 128, 1 gives the prefill GEMM and 0 or 2 the GEMV.
  *   rw     path 0: row tiles per workgroup, 1, 2 or 4 (the workgroup's 4
- *          waves are rw row tiles x 4/rw waves sharing one);
+ *          waves are rw row tiles x 4/rw waves sharing one), or 8: 4 row
+ *          tiles x 2 waves (512 threads; needs K-splits of at least 2
+ *          k-tiles, else 4 is taken);
  *          path 2: waves per workgroup sharing its one row tile, 4, 8 or
  *          16 (at most 8 when M > 16);
  *          path 1 (forced): 1 or 2 = tiles of 64 or 128 tokens;
  *          0 (or a value the path does not take) = built-in choice.
  *   ch     path 0: k-tiles (128 inputs) per LDS table stage: 1, 2, 4
- *          or 8, capped so one stage stays within 32 KB;
+ *          or 8, capped so one stage stays within 32 KB (with rw = 8 at
+ *          least 2, one per wave, up to 64 KB);
  *          path 1 (forced): 2 or 4 k-phases (4: tiles 128 weight rows
  *          wide, each workgroup's K split four ways);
  *          0 = built-in.

@@ -143,6 +143,12 @@ def test_plan_override_changes_plan_and_workspace():
         assert bw.workspace_bytes(1, 4096, 4096) == 4096 * 8
         bw.plan_override("lut_gemv", splits=1)
         assert bw.workspace_bytes(1, 4096, 4096) == 0
+        bw.plan_override("lut_gemv", rw=8, splits=4)       # 4 row tiles x 2 waves
+        p = bw.plan(16, 4096, 4096)
+        assert p["block"] == 512 and p["grid"] == 16 * 4 and p["lds_bytes"] == 2 * 32 * 8 * 32 * 4
+        bw.plan_override("lut_gemv", rw=8, splits=32)      # 1-k-tile splits: 4 waves instead
+        p = bw.plan(16, 4096, 4096)
+        assert p["block"] == 256 and p["grid"] == 16 * 32
         bw.plan_override("decode_mfma_gemv", rw=4, splits=4)
         p = bw.plan(3, 4096, 4096)
         assert p["path"] == "decode_mfma_gemv" and p["grid"] == 64 * 4 and p["block"] == 256

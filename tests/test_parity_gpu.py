@@ -221,7 +221,7 @@ def test_gemm_edges(orc, packed_cases, M, N, K):
 
 
 PLANS = [(4, 1, 0), (4, 2, 3), (2, 2, 0), (2, 4, 2), (1, 1, 0), (1, 2, 5), (1, 8, 1), (4, 8, 1),
-         (2, 1, 7)]
+         (2, 1, 7), (8, 0, 0), (8, 2, 3), (8, 4, 2), (8, 0, 9)]   # 8: 4 row tiles x 2 waves
 
 
 @pytest.mark.parametrize("rw,ch,splits", PLANS)
@@ -740,7 +740,7 @@ def test_linear_edges(orc, packed_cases, M, N, K):
 @pytest.mark.parametrize("path,rw,splits", [("decode_mfma_gemv", 4, 1), ("decode_mfma_gemv", 4, 3),
                                             ("decode_mfma_gemv", 16, 2), ("decode_mfma_gemv", 8, 9),
                                             ("lut_gemv", 0, 0), ("lut_gemv", 1, 3), ("lut_gemv", 2, 1),
-                                            ("lut_gemv", 4, 9), ("decode_mfma", 0, 0)])
+                                            ("lut_gemv", 4, 9), ("lut_gemv", 8, 3), ("decode_mfma", 0, 0)])
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_linear_plans(orc, packed_cases, path, rw, splits, M):
     """Fused (both GEMVs) and unfused (prefill kernel) forms agree with the
@@ -901,7 +901,7 @@ def ragged_cases(orc):
 
 
 RAGGED_PLANS = [(None, 0, 0), ("decode_mfma_gemv", 4, 3), ("decode_mfma_gemv", 16, 1),
-                ("decode_mfma_gemv", 8, 2), ("lut_gemv", 0, 0), ("lut_gemv", 1, 3),
+                ("decode_mfma_gemv", 8, 2), ("lut_gemv", 0, 0), ("lut_gemv", 1, 3), ("lut_gemv", 8, 2),
                 ("decode_mfma", 0, 0), ("decode_mfma", 1, 0), ("decode_mfma", 2, 0)]
 
 
