@@ -134,6 +134,39 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
     __syncthreads();
   }
 
+  // Table-build items per thread and stage: item = (segment, pair, zero
+  // position z).  A thread's activation words for a stage's items (two
+  // tokens' 4 inputs each) are loaded together, a stage ahead, so the build
+  // waits for at most one memory round trip instead of one per item.
+  constexpr int kItems = (CH * 32 * MP * 4 + NT - 1) / NT;
+  auto load_x = [&](int st, int (&x0)[kItems], int (&x1)[kItems]) {
+    const int kt_s = kt_begin + st * CH;
+    const int items = min(CH, kt_end - kt_s) * 32 * MP * 4;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int it = threadIdx.x + NT * i;
+      const int rest = it >> 2;       // segment * MP + pair
+      const int pair = rest % MP;
+      const int seg = rest / MP;
+      const int k = kt_s * kTileK + 4 * seg;
+      const int m0 = 2 * pair, m1 = 2 * pair + 1;
+      // segments past K (padding of a ragged last k-tile) get zero tables
+      x0[i] = 0;
+      x1[i] = 0;
+      if (it < items) {
+        if constexpr (FQ) {
+          if (m0 < M && k < K) x0[i] = quant_word(a.xf + (size_t)m0 * K + k, fq_s[m0]);
+          if (m1 < M && k < K) x1[i] = quant_word(a.xf + (size_t)m1 * K + k, fq_s[m1]);
+        } else {
+          if (m0 < M && k < K) x0[i] = *reinterpret_cast<const int*>(a.x + (size_t)m0 * K + k);
+          if (m1 < M && k < K) x1[i] = *reinterpret_cast<const int*>(a.x + (size_t)m1 * K + k);
+        }
+      }
+    }
+  };
+  int xw0[kItems], xw1[kItems];
+  load_x(0, xw0, xw1);
+
   int acc[2 * MP];
 #pragma unroll
   for (int m = 0; m < 2 * MP; ++m) acc[m] = 0;
@@ -141,27 +174,20 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
   for (int st = 0; st < nst; ++st) {
     const int kt_s = kt_begin + st * CH;
     const int nch = min(CH, kt_end - kt_s);
-    if (st > 0) __syncthreads();  // previous stage's lookups are done
+    // barriers on LDS only: __syncthreads() would also wait for the loads
+    // of the next stage's activations and codes in flight
+    if (st > 0) lds_barrier();    // previous stage's lookups are done
 
-    // tables of this stage: item = (segment, pair, zero position z)
+    // tables of this stage, from the activation words loaded for it
     {
       const int items = nch * 32 * MP * 4;
-      for (int it = threadIdx.x; it < items; it += NT) {
+#pragma unroll
+      for (int i = 0; i < kItems; ++i) {
+        const int it = threadIdx.x + NT * i;
+        if (it >= items) continue;
         const int z = it & 3;
         const int rest = it >> 2;       // segment * MP + pair
-        const int pair = rest % MP;
-        const int seg = rest / MP;
-        const int k = kt_s * kTileK + 4 * seg;
-        const int m0 = 2 * pair, m1 = 2 * pair + 1;
-        // segments past K (padding of a ragged last k-tile) get zero tables
-        int x0 = 0, x1 = 0;
-        if constexpr (FQ) {
-          if (m0 < M && k < K) x0 = quant_word(a.xf + (size_t)m0 * K + k, fq_s[m0]);
-          if (m1 < M && k < K) x1 = quant_word(a.xf + (size_t)m1 * K + k, fq_s[m1]);
-        } else {
-          if (m0 < M && k < K) x0 = *reinterpret_cast<const int*>(a.x + (size_t)m0 * K + k);
-          if (m1 < M && k < K) x1 = *reinterpret_cast<const int*>(a.x + (size_t)m1 * K + k);
-        }
+        const int x0 = xw0[i], x1 = xw1[i];
         // the three kept positions in order: ja < jb < jc, none equal to z
         const int ja = z == 0 ? 1 : 0;
         const int jb = z <= 1 ? 2 : 1;
@@ -179,7 +205,8 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
                             __builtin_bit_cast(uint32_t, p3), __builtin_bit_cast(uint32_t, zero - p3));
       }
     }
-    __syncthreads();
+    if (st + 1 < nst) load_x(st + 1, xw0, xw1);
+    lds_barrier();
 
     uint32_t nxt[CPW][5];
     if (st + 1 < nst) load_stage(st + 1, nxt);
