@@ -75,8 +75,14 @@ struct Tiling {
   static constexpr int kABufs = kPair ? 4 : (BM == 128 && KP == 4 ? 2 : 3);
   static constexpr int kRT = kThreads / 64 / KP;       // row tiles per workgroup (4 or 2)
   static constexpr int kBN = kRT * kTileRows;          // workgroup tile width (256 or 128 weight rows)
-  static constexpr int kOutLd = kBN + 16;              // words per row of the epilogue tiles (the 4
-                                                       // row groups of an MFMA block hit 4 bank quarters)
+  // Words per row of the epilogue tiles.  One sums write (an accumulator
+  // register of every lane) puts rows r, r+4, r+8, r+12 of an MFMA block in
+  // lanes 0-15, 16-31, 32-47, 48-63; a pitch of 4 (mod 16) words spaces
+  // those rows 16 banks apart, so no two lanes of a write share a bank.  (At
+  // kBN + 16 the four rows were 1088 words, a multiple of 64, apart: measured
+  // with the padded pitch, M=512, N=14336, K=4096 31.4 -> 31.1 us; M=256
+  // 20.5 -> 19.9; M=128 13.7 -> 13.5.)
+  static constexpr int kOutLd = kBN + 4;
   static constexpr int kLdsOut = KP * 32 * kOutLd * 4; // epilogue tiles (32 rows, every phase)
   static constexpr int kMT = BM / 16;                  // row blocks per wave (8 or 4)
   static constexpr int kAStage = BM * kBK;             // activation bytes per k-step
