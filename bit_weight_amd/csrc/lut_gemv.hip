@@ -267,6 +267,13 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
   const int n = rt * kTileRows + lane;
   if (n >= N) return;                           // rows past N: padding, never stored
   const float al = a.y ? a.alpha[n] : 0.0f;
+  // The tokens' scales are loaded here, with alpha, before any atomic or
+  // store: the memory counter counts stores too, so a scale loaded after
+  // one token's store would make the next store wait for it, and the lane's
+  // M stores would leave one round trip apart.
+  float sxm[2 * MP];
+#pragma unroll
+  for (int m = 0; m < 2 * MP; ++m) sxm[m] = !FQ && a.y && m < M ? a.s_x[m] : 0.0f;
   // every token's atomic is issued before any result is used: one memory
   // round trip per lane whatever M is
   int total[2 * MP];
@@ -299,12 +306,20 @@ __global__ __launch_bounds__(64 * RW * KW) void lut_gemv_kernel(const uint8_t* p
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  // every output is formed before the first store (the empty asm keeps
+  // each product out of the store branches), so the one wait for alpha
+  // comes before any store rather than between them
+  float yv[2 * MP];
+#pragma unroll
+  for (int m = 0; m < 2 * MP; ++m) {
+    yv[m] = ((float)total[m] * (FQ ? fq_s[m] : sxm[m])) * al;
+    asm volatile("" : "+v"(yv[m]));
+  }
 #pragma unroll
   for (int m = 0; m < 2 * MP; ++m) {
     if (m >= M || !last[m]) continue;
     if (a.y) {
-      const float t = (float)total[m] * (FQ ? fq_s[m] : a.s_x[m]);
-      a.y[(size_t)m * N + n] = t * al;
+      a.y[(size_t)m * N + n] = yv[m];
     } else {
       a.acc[(size_t)m * N + n] = total[m];
     }

@@ -439,6 +439,12 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const uint8_t* pack
   float4 al4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (want_y && n < N) al4 = make_float4(a.alpha[n], a.alpha[n + 1], a.alpha[n + 2], a.alpha[n + 3]);
   if (want_y && tid < kBM) sxs[tid] = a.s_x[min(m0 + tid, M - 1)];
+  // The scale loads complete here, before the first output store.  The
+  // memory counter counts stores as well as loads, so a wait for alpha
+  // placed after a store also waits for that store; left to itself the
+  // compiler puts such a wait before every row's scaling, and the tile's
+  // 16 rows of stores then leave one round trip at a time.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   int* ot = reinterpret_cast<int*>(lds);       // [phase][32][kOutLd] sums
   int* mine = ot + kh * 32 * kOutLd;
 #pragma unroll

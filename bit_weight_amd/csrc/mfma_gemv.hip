@@ -396,6 +396,17 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
   const int n = rt * kTileRows + lane;
   const bool n_ok = n < N;                            // rows past N: padding, never stored
   const float al = a.y && n_ok ? a.alpha[n] : 0.0f;
+  // the scales of this wave's tokens, loaded with alpha before any atomic
+  // or store (the memory counter counts stores too: a scale loaded after a
+  // store would make the next store wait for that one)
+  float sxm[MB][TPW];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int m = 16 * b + q * TPW + i;
+      sxm[b][i] = !FQ && a.y && q * TPW < MT && m < M ? a.s_x[m] : 0.0f;
+    }
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
     if (b > 0) __syncthreads();   // the previous block's sums are read
@@ -444,13 +455,22 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(const uint8_t* packe
           __hip_atomic_store(cells + (size_t)m * N + n, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+    // every output formed before the first store (the empty asm keeps each
+    // product out of the store branches): the wait for alpha then comes
+    // once, not between stores
+    float yv[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int m = min(16 * b + q * TPW + i, MT - 1);
+      yv[i] = ((float)total[i] * (FQ ? sred[KW * MT + m] : sxm[b][i])) * al;
+      asm volatile("" : "+v"(yv[i]));
+    }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int m = 16 * b + q * TPW + i;
       if (m >= M || !n_ok || !last[i]) continue;
       if (a.y) {
-        const float tv = (float)total[i] * (FQ ? sred[KW * MT + m] : a.s_x[m]);
-        a.y[(size_t)m * N + n] = tv * al;
+        a.y[(size_t)m * N + n] = yv[i];
       } else {
         a.acc[(size_t)m * N + n] = total[i];
       }
