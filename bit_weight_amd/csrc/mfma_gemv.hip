@@ -502,15 +502,17 @@ hipError_t launch_kw(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     // one token: its split's int8 x staged in LDS (measured 2-4 % faster at
     // M=1; at M=4 the chunk loads, sized for the longest split, cost more
     // than the per-step loads they replace)
-    // straight-line steps for one token block with no K-split and 4 to 8
-    // k-tiles per wave (measured at M=8, K=8192, N=28672: 13.4 -> 12.2 us;
-    // with fewer k-tiles the loop never takes its back edge, and with
-    // several token blocks it was 2 % slower), with two register stages
-    // (against four, measured on MI355X: M=8, K=8192, N=28672 12.5 ->
-    // 11.9 us; M=16, K=4096, N=14336 6.8 -> 6.1; M=1, K=4096, N=11008
-    // 4.99 -> 4.73; no shape slower)
+    // straight-line steps for one token block and 4 to 8 k-tiles per wave
+    // (measured at M=8, K=8192, N=28672: 13.4 -> 12.2 us; with fewer k-tiles
+    // the loop never takes its back edge, and with several token blocks it
+    // was 2 % slower), with two register stages (against four, measured on
+    // MI355X: M=8, K=8192, N=28672 12.5 -> 11.9 us; M=16, K=4096, N=14336
+    // 6.8 -> 6.1; M=1, K=4096, N=11008 4.99 -> 4.73; no shape slower), also
+    // under a K-split (the long-K plans split K to reach this form; N=8192,
+    // K=28672, 4 splits of 7 k-tiles per wave: M=1 11.4 -> 10.2 us, M=4
+    // 11.7 -> 10.8, M=8 11.8 -> 11.4)
     const int nkw = (p.kt_per_split + KW - 1) / KW;
-    const bool sl4 = p.splits == 1 && nkw >= 4 && nkw <= kSL;
+    const bool sl4 = nkw >= 4 && nkw <= kSL;
 #define SHERRY_GEMV(MT_, MB_, ST_, SX_, SL_) \
   launch_product_kernel(mfma_gemv_kernel<KW, MT_, MB_, false, FMT, ST_, 1, SX_, SL_>, grid, block, 0, stream, a, p.splits, p.kt_per_split)
     if (a.M <= 1 && p.kt_per_split <= kFuseMaxSpan) {
