@@ -77,9 +77,14 @@ GemmPlan plan_mfma_gemv(int M, int N, int K) {
     // straight-line form's limit), 16 above 8 tokens, where each split's
     // cells cost more (measured at N=8192, K=28672: M=1 16.6 -> 11.6 us,
     // M=8 17.1 -> 12.6, M=16 20.3 -> 14.7; at K <= 8192 no split stays the
-    // best).  Several token blocks keep one split (unmeasured at long K).
+    // best), unless the row tiles fill at most half the CUs: there the
+    // splits' extra workgroups are worth their cells (N=8192 above 8 tokens,
+    // 8 against 16 k-tiles per wave: M=10, K=14336 11.6 -> 8.6 us; M=16,
+    // K=28672 13.9 -> 13.6; at N=14336, 224 row tiles, M=16, K=16384 a
+    // split made it 13.3 -> 14.4).  Several token blocks keep one split
+    // (unmeasured at long K).
     if (M <= 16) {
-      const int per_split = kw * (M > 8 ? 16 : 8);
+      const int per_split = kw * (M > 8 && 2 * RT > kCUs ? 16 : 8);
       splits = (KT + per_split - 1) / per_split;
     }
   } else if (M > 8) {
