@@ -81,11 +81,17 @@ GemmPlan plan_mfma_gemv(int M, int N, int K) {
     // splits' extra workgroups are worth their cells (N=8192 above 8 tokens,
     // 8 against 16 k-tiles per wave: M=10, K=14336 11.6 -> 8.6 us; M=16,
     // K=28672 13.9 -> 13.6; at N=14336, 224 row tiles, M=16, K=16384 a
-    // split made it 13.3 -> 14.4).  Several token blocks keep one split
-    // (unmeasured at long K).
+    // split made it 13.3 -> 14.4).
     if (M <= 16) {
       const int per_split = kw * (M > 8 && 2 * RT > kCUs ? 16 : 8);
       splits = (KT + per_split - 1) / per_split;
+    } else if (2 * RT <= kCUs && KT > 8 * kw) {
+      // several token blocks at long K on row tiles that fill at most half
+      // the CUs: split K so the grid fills one round (N=8192: M=32, K=28672
+      // 25.4 -> 18.4 us; M=64, K=14336 23.0 -> 19.6; M=48, K=11008 18.4 ->
+      // 15.9; four splits, two rounds, were slower than none, and at
+      // N=14336, 224 row tiles, two splits made M=32, K=16384 17.0 -> 24.8)
+      splits = kCUs / RT;
     }
   } else if (M > 8) {
     // KT / (3 kw), rounded, but no more workgroups than one round of CUs: a
